@@ -1,0 +1,117 @@
+"""Pins of the oracle's routing and permutation against brute force, closed
+forms and invariants."""
+
+import math
+
+import numpy as np
+import pytest
+
+from oracle import permute as operm
+from oracle import route as oroute
+
+
+def brute_order(row):
+    """Experts best-first by Python's sort on (-logit, index); NaN ranks as -inf."""
+    key = [(-(-math.inf if math.isnan(v) else v), i) for i, v in enumerate(row)]
+    return [i for _, i in sorted(key)]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_topk_ids_match_brute_force_with_many_ties(seed):
+    rng = np.random.default_rng(seed)
+    T, E = 40, int(rng.integers(2, 40))
+    k = int(rng.integers(1, E + 1))
+    # few distinct values -> many ties; include signed zeros, -inf and NaN
+    pool = np.array([0.0, -0.0, 1.5, -2.0, 3.25, -math.inf, math.nan], np.float32)
+    logits = rng.choice(pool, size=(T, E)).astype(np.float32)
+    logits[:, 0] = 0.5                               # at least one finite logit per row
+    ids, w = oroute.route_topk(logits, k)
+    for t in range(T):
+        assert list(ids[t]) == brute_order(logits[t])[:k]
+
+
+def test_topk_k1_is_argmax_lowest_index_and_kE_is_full_order():
+    l = np.array([[1.0, 3.0, 3.0, 2.0], [0.0, 0.0, 0.0, 0.0]], np.float32)
+    ids, w = oroute.route_topk(l, 1)
+    assert ids[:, 0].tolist() == [1, 0] and np.all(w == 1.0)
+    ids, _ = oroute.route_topk(l, 4)
+    assert ids.tolist() == [[1, 2, 3, 0], [0, 1, 2, 3]]
+
+
+def test_equal_logits_give_first_k_and_uniform_weights():
+    ids, w = oroute.route_topk(np.full((3, 10), 0.7, np.float32), 4)
+    assert ids.tolist() == [[0, 1, 2, 3]] * 3
+    assert np.all(w == np.float32(0.25))
+
+
+def test_signed_zero_ties_and_nan_ranks_last():
+    ids, _ = oroute.route_topk(np.array([[-0.0, 0.0, -1.0]], np.float32), 2)
+    assert ids.tolist() == [[0, 1]]
+    ids, _ = oroute.route_topk(np.array([[0.0, -0.0, -1.0]], np.float32), 2)
+    assert ids.tolist() == [[0, 1]]
+    ids, w = oroute.route_topk(np.array([[math.nan, 1.0, 0.0]], np.float32), 3)
+    assert ids.tolist() == [[1, 2, 0]]
+    assert w[0, 2] == 0.0
+
+
+def test_two_expert_weight_is_a_sigmoid_of_the_gap():
+    rng = np.random.default_rng(1)
+    l = (rng.standard_normal((50, 6)) * 3).astype(np.float32)
+    ids, w = oroute.route_topk(l, 2)
+    for t in range(50):
+        a, b = float(l[t, ids[t, 0]]), float(l[t, ids[t, 1]])
+        w0 = 1.0 / (1.0 + math.exp(-(a - b)))           # closed form of the renormalised pair
+        assert abs(float(w[t, 0]) - w0) <= 2 ** -24
+        assert abs(float(w[t, 1]) - (1 - w0)) <= 2 ** -24
+
+
+def test_weights_sum_to_one_and_do_not_increase():
+    rng = np.random.default_rng(2)
+    l = (rng.standard_normal((300, 384)) * 1.6).astype(np.float32)
+    ids, w = oroute.route_topk(l, 8)
+    assert np.all(np.abs(w.astype(np.float64).sum(1) - 1) <= 8 * 2 ** -24)
+    assert np.all(np.diff(w, axis=1) <= 0)
+    # the chosen logits are the 8 largest
+    kth = np.sort(l, axis=1)[:, -8]
+    assert np.all(np.take_along_axis(l, ids, 1) >= kth[:, None])
+
+
+def test_shift_invariance():
+    rng = np.random.default_rng(4)
+    l = rng.integers(-20, 20, (30, 16)).astype(np.float32)
+    i1, w1 = oroute.route_topk(l, 5)
+    i2, w2 = oroute.route_topk(l + np.float32(64), 5)
+    assert np.array_equal(i1, i2) and np.allclose(w1, w2, rtol=0, atol=2 ** -22)
+
+
+def test_empty_tokens():
+    ids, w = oroute.route_topk(np.zeros((0, 8), np.float32), 2)
+    assert ids.shape == (0, 2) and w.shape == (0, 2)
+
+
+# ---------------------------------------------------------------------------
+# permute
+
+
+@pytest.mark.parametrize("T,E,k,seed", [(16, 8, 2, 0), (1, 4, 4, 1), (37, 64, 8, 2),
+                                        (200, 384, 8, 3), (0, 5, 2, 4), (9, 3, 1, 5)])
+def test_permute_matches_stable_argsort_construction(T, E, k, seed):
+    rng = np.random.default_rng(seed)
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]) if T else np.zeros((0, k), int)
+    d = operm.permute(ids, E)
+    flat = ids.reshape(-1)
+    # independent construction: stable sort of the expert ids
+    order = np.argsort(flat, kind="stable")
+    counts = np.bincount(flat, minlength=E)
+    assert np.array_equal(d["counts"], counts)
+    assert np.array_equal(d["offsets"], np.concatenate([[0], np.cumsum(counts)]))
+    assert np.array_equal(d["sorted_pairs"], order)
+    assert np.array_equal(d["sorted_pairs"][d["pair_to_row"]], np.arange(T * k))
+    for e in range(E):
+        seg = d["sorted_pairs"][d["offsets"][e]:d["offsets"][e + 1]]
+        assert np.all(flat[seg] == e) and np.all(np.diff(seg) > 0)
+
+
+def test_permute_rejects_out_of_range():
+    with pytest.raises(ValueError):
+        operm.permute(np.array([[0, 5]]), 4)
