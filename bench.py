@@ -1,0 +1,234 @@
+"""Benchmark of the MXFP4 MoE expert layer on one MI355X.
+
+One step = the whole layer (moe_route_topk -> moe_permute ->
+moe_mxfp4_gate_up_swiglu -> moe_mxfp4_down -> moe_combine) over one batch of
+synthetic tokens, inputs resident in HBM.  Default workload: the page-shaped
+layer (hidden 6144, 384 experts, top-8, intermediate 2048, MXFP4 block 32)
+verifying one sequence's 8-token draft block.  Two copies of the expert
+weights alternate between steps so the 256 MB last-level cache cannot serve
+them.
+
+Prints ONE JSON line on stdout; diagnostics go to stderr.
+  value       tokens/s of the whole layer
+  roofline    the gate/up contraction (the kernel that streams 2/3 of the
+              weight bytes): algorithmic bytes per launch / its mean duration
+              from HIP events recorded around it on its stream inside the
+              timed region, against 8 TB/s
+  cpu_baseline  the float64 CPU oracle on a bounded sample of the same tokens
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MXFP4 MoE layer tokens/s + effective weight GB/s (% HBM peak) on 1 MI355X"
+HBM_PEAK_GBPS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("expert_stream.hip", "common.hpp"):
+        with open(os.path.join(ROOT, "mxfp4_moe_expert_route_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 PMC summary, or None
+    when it is missing or was taken from another version of the kernel."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get("%s@%s" % (kernel, workload))
+    if not rec or rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg, x_bits, logits, whost, budget_s):
+    """Time the oracle on growing token subsets until `budget_s` is spent."""
+    from oracle import layer as olayer
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    done, elapsed = 0, 0.0
+    step = max(1, min(cfg.T, 2))
+    while done < cfg.T and elapsed < budget_s:
+        tok = np.arange(done, min(cfg.T, done + step))
+        t0 = time.perf_counter()
+        olayer.layer_forward(x_bits, logits, whost["w13_codes"], whost["w13_scales"],
+                             whost["w2_codes"], whost["w2_scales"], cfg.k, tokens=tok)
+        elapsed += time.perf_counter() - t0
+        done += len(tok)
+    return {"value": done / elapsed, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": "%d of %d tokens of %s, whole layer (routing of all tokens, float64 "
+                      "dequantised expert FFNs, combine) with numpy on the host, %.1f s"
+                      % (done, cfg.T, cfg.name, elapsed)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--config", default="verify_t8")
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of oracle work for cpu_baseline (0 disables)")
+    ap.add_argument("--breakdown", action="store_true", help="per-kernel times on stderr")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py: this build runs on exactly one GPU; --gpus %d is not supported "
+              "(the layer is measured on one MI355X)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import mxfp4_moe_expert_route_amd as mm
+    import workloads
+
+    cfg = workloads.CONFIGS[args.config]
+    steps = args.steps or (200 if cfg.T <= 512 else 30)
+    warmup = args.warmup if args.warmup is not None else (20 if cfg.T <= 512 else 5)
+    dev = torch.device("cuda:0")
+    mm._lib.lib()
+
+    t0 = time.perf_counter()
+    whost = workloads.all_weights(cfg, 0)
+    x_bits = workloads.gen_x_bits(cfg, 0)
+    logits_h = workloads.gen_logits(cfg, x_bits, 0)
+    log("inputs generated in %.1f s (%.2f GB of expert weights)"
+        % (time.perf_counter() - t0, cfg.E * cfg.expert_bytes() / 1e9))
+    names = ("w13_codes", "w13_scales", "w2_codes", "w2_scales")
+    w0 = {k: torch.from_numpy(whost[k]).to(dev) for k in names}
+    w1 = {k: v.clone() for k, v in w0.items()}           # second copy for cache rotation
+    wsets = (w0, w1)
+    x = torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    logits = torch.from_numpy(logits_h).to(dev)
+    T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
+    b = mm.LayerBuffers(T, H, I, E, k, dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        w = wsets[i & 1]
+        mm.moe_route_topk(logits, k, b.topk_ids, b.topk_w)
+        mm.moe_permute(b.topk_ids, E, b.counts, b.offsets, b.sorted_pairs, b.pair_to_row,
+                       b.workspace)
+        if ev is not None:
+            ev[0].record(stream)
+        mm.moe_mxfp4_gate_up_swiglu(x, b.sorted_pairs, b.offsets, k, w["w13_codes"],
+                                    w["w13_scales"], b.h)
+        if ev is not None:
+            ev[1].record(stream)
+        mm.moe_mxfp4_down(b.h, b.offsets, k, w["w2_codes"], w["w2_scales"], b.y)
+        mm.moe_combine(b.y, b.topk_w, b.pair_to_row, b.out)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(steps):
+        step(i, evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t_start.elapsed_time(t_end) / steps
+    gu_ms = float(np.mean([a.elapsed_time(bb) for a, bb in evs]))
+    log("wall %.3f ms/step, events %.3f ms/step, gate_up %.3f ms"
+        % (wall * 1e3 / steps, ms_step, gu_ms))
+
+    counts = b.counts.cpu().numpy()
+    touched = int((counts > 0).sum())
+    w13_bytes = 2 * I * H // 2 + 2 * I * H // 32
+    w2_bytes = H * I // 2 + H * I // 32
+    layer_weight_bytes = touched * (w13_bytes + w2_bytes)
+    gu_bytes = touched * w13_bytes + T * H * 2          # weights streamed + x read once
+    flops = 6.0 * T * k * H * I
+    eff_gbps = layer_weight_bytes / (ms_step * 1e-3) / 1e9
+    gu_gbps = gu_bytes / (gu_ms * 1e-3) / 1e9
+    tokens_per_s = T / (ms_step * 1e-3)
+
+    if args.breakdown:
+        names_k = ("route", "permute", "gate_up", "down", "combine")
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(20)]
+        for r in range(20):
+            w = wsets[r & 1]
+            e = ev[r]
+            e[0].record(stream)
+            mm.moe_route_topk(logits, k, b.topk_ids, b.topk_w)
+            e[1].record(stream)
+            mm.moe_permute(b.topk_ids, E, b.counts, b.offsets, b.sorted_pairs, b.pair_to_row,
+                           b.workspace)
+            e[2].record(stream)
+            mm.moe_mxfp4_gate_up_swiglu(x, b.sorted_pairs, b.offsets, k, w["w13_codes"],
+                                        w["w13_scales"], b.h)
+            e[3].record(stream)
+            mm.moe_mxfp4_down(b.h, b.offsets, k, w["w2_codes"], w["w2_scales"], b.y)
+            e[4].record(stream)
+            mm.moe_combine(b.y, b.topk_w, b.pair_to_row, b.out)
+            e[5].record(stream)
+        torch.cuda.synchronize()
+        for i, n in enumerate(names_k):
+            t = np.median([ev[r][i].elapsed_time(ev[r][i + 1]) for r in range(20)])
+            log("  %-8s %8.1f us" % (n, t * 1e3))
+
+    cpu = None
+    if args.cpu_budget > 0:
+        cpu = cpu_baseline(cfg, x_bits, logits_h, whost, args.cpu_budget)
+        log("cpu baseline: %.3f tokens/s (%s)" % (cpu["value"], cpu["sample"]))
+
+    traffic = measured_traffic("moe_mxfp4_gate_up_swiglu", cfg.name)
+    line = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "tokens": T, "hidden": H, "intermediate": I,
+                   "experts": E, "top_k": k, "weight_format": "mxfp4 (E2M1, E8M0 per 32)",
+                   "touched_experts": touched, "weight_bytes_touched": layer_weight_bytes,
+                   "seed": 0, "parallelism": "none (1 GPU)"},
+        "effective_weight_GBps": round(eff_gbps, 1),
+        "hbm_frac_layer": round(eff_gbps / HBM_PEAK_GBPS, 4),
+        "mfma_frac_layer": round(flops / (ms_step * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+        "roofline": {"kernel": "moe_mxfp4_gate_up_swiglu", "bound": "hbm",
+                     "achieved": round(gu_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gu_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic, "algorithmic_bytes": gu_bytes,
+                     "mean_launch_ms": round(gu_ms, 5)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

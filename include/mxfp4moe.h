@@ -1,0 +1,201 @@
+/*
+ * mxfp4moe.h — C ABI of the MXFP4 Mixture-of-Experts expert layer for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The layer: each token's router logits pick k of E experts; each chosen
+ * expert is a SwiGLU FFN whose weights are stored in MXFP4 (4-bit E2M1
+ * elements, one E8M0 power-of-two scale per 32 consecutive elements along the
+ * reduction axis); activations are bf16, accumulation fp32; the k expert
+ * outputs are mixed with the routing weights.  The pages this follows
+ * ("MiMo-V2.5-Pro-FP4-DFlash" model card, §1 Introduction, §2 "FP4
+ * Quantization", §3 DFlash, §4 "Model Summary"; nxbn.cn article
+ * "MiMo-V2.5-Pro-FP4-DFlash万亿参数大模型推理效率的终极突破", sub-sections
+ * "量化策略的智能选择" and "架构设计与配置详解") fix MXFP4 with block 32 for
+ * the experts only, 384 experts with 8 active per token, hidden size 6144,
+ * and verification of an 8-token draft block per sequence per step.  The
+ * encodings are those of the OCP MX v1.0 specification.  The SwiGLU form,
+ * the softmax-renormalised routing rule, the bit layout and the rounding of
+ * the intermediate h to bf16 are readings of what the pages leave open; they
+ * are stated at each call below.
+ *
+ * Conventions for every call
+ *   - All array arguments are DEVICE pointers, allocated and owned by the
+ *     caller.  The library never allocates or frees device memory and keeps
+ *     no state between calls; calls are thread-safe.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Each call only enqueues kernels on it and returns; there is no host
+ *     synchronisation.  Results are valid once the stream reaches them.
+ *   - Errors are returned as a negative status (MXM_ERR_*).  Argument checks
+ *     are done on the host before anything is enqueued; on an error nothing
+ *     is launched and no output is touched.  MXM_ERR_LAUNCH reports a HIP
+ *     launch failure after the checks passed.
+ *   - An empty problem (T == 0, rows == 0) is a no-op that returns MXM_OK;
+ *     its pointers may then be NULL.
+ *   - Integer indices are int32 (T*k < 2^31).  H and I must be multiples of
+ *     32 (no partial MX blocks).  1 <= k <= min(E, 32), E <= 1024.
+ *   - Pointer alignment: codes, x (pack input), y (unpack output), x_bf16,
+ *     h_bf16, y and out 16 bytes; everything else 4 bytes.
+ *     Rows are densely packed (the leading stride is the row length).
+ */
+#ifndef MXFP4MOE_H
+#define MXFP4MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum mxm_status {
+  MXM_OK = 0,
+  MXM_ERR_NULL = -1,          /* a required pointer is NULL */
+  MXM_ERR_SHAPE = -2,         /* a size is out of range (K%32, k>E, E>1024, ...) */
+  MXM_ERR_DTYPE = -3,         /* unknown dtype code */
+  MXM_ERR_ALIGN = -4,         /* a pointer is not aligned as stated above */
+  MXM_ERR_LAUNCH = -5,        /* a kernel launch failed (HIP error) */
+  MXM_ERR_UNIMPLEMENTED = -6, /* reserved */
+  MXM_ERR_WORKSPACE = -7      /* workspace smaller than the call needs */
+};
+
+enum mxm_dtype { MXM_F32 = 0, MXM_BF16 = 1 };
+
+/* Library version as 10000*major + 100*minor + patch. */
+int mxm_version(void);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* mxm_status_string(int status);
+
+/*
+ * mxfp4_pack — quantise a row-major matrix to MXFP4.
+ *   x       [rows, K] f32 or bf16 (x_dtype = MXM_F32 / MXM_BF16), read only
+ *   codes   [rows, K/2] uint8, written: byte j of a row holds element 2j in
+ *           bits 3..0 and element 2j+1 in bits 7..4 (reading: the pages do
+ *           not give the nibble order)
+ *   scales  [rows, K/32] uint8 E8M0, written
+ * Conversion per 32-element block (OCP MX v1.0; the pages name MXFP4 with
+ * block 32 — model card §2 — and give no rounding rule): scale exponent
+ * e = clamp(floor(log2(max|x|)) - 2 + 127, 0, 254); each x*2^(127-e) is
+ * rounded to the nearest E2M1 value, ties to the even code, saturating at 6;
+ * the code's sign bit is x's sign bit.  An all-zero block gets e = 0; a block
+ * holding NaN or Inf gets e = 0xFF and zero codes.  Bit-exact and
+ * deterministic.  Requires K % 32 == 0; rows, K >= 0.
+ */
+int mxfp4_pack(const void* x, int x_dtype, int64_t rows, int64_t K,
+               uint8_t* codes, uint8_t* scales, void* stream);
+
+/*
+ * mxfp4_unpack — dequantise MXFP4 to f32 or bf16.
+ *   codes [rows, K/2], scales [rows, K/32] as written by mxfp4_pack
+ *   y     [rows, K] f32 or bf16 (y_dtype), written
+ * y = E2M1(code) * 2^(e-127), computed exactly and rounded to the output type
+ * (exact for every finite result, subnormals included; f32 overflows to Inf
+ * only for e >= 253).  A scale byte 0xFF gives a quiet NaN for the block.
+ */
+int mxfp4_unpack(const uint8_t* codes, const uint8_t* scales, int64_t rows,
+                 int64_t K, void* y, int y_dtype, void* stream);
+
+/*
+ * moe_route_topk — choose k experts per token.
+ *   logits  [T, E] f32, read (the router projection is upstream of this call)
+ *   topk_ids[T, k] int32, written: experts by descending logit, the lower
+ *           index first on equal logits; -0.0 equals +0.0; NaN ranks as -inf
+ *   topk_w  [T, k] f32, written: softmax over all E experts renormalised over
+ *           the k chosen, i.e. w_j = exp(l_j - l_1) / sum_j' exp(l_j' - l_1)
+ * The pages give 384 experts and 8 active per token (nxbn.cn article,
+ * "架构设计与配置详解") and no scoring rule; the rule above is the reading.
+ * Ids are deterministic and bit-exact; a row with a +Inf logit or with no
+ * finite logit has undefined weights.
+ */
+int moe_route_topk(const float* logits, int T, int E, int k,
+                   int32_t* topk_ids, float* topk_w, void* stream);
+
+/* Workspace moe_permute needs for these sizes (currently always 0). */
+size_t moe_permute_workspace_bytes(int T, int E, int k);
+
+/*
+ * moe_permute — group token-expert pairs by expert.
+ *   topk_ids     [T, k] int32, read; each in [0, E)
+ *   counts       [E]   int32, written: pairs routed to each expert
+ *   offsets      [E+1] int32, written: exclusive prefix sum of counts
+ *   sorted_pairs [T*k] int32, written: pair ids p = t*k + j, expert segments
+ *                in expert order, ascending p within a segment
+ *   pair_to_row  [T*k] int32, written: inverse of sorted_pairs
+ *   workspace    device scratch of moe_permute_workspace_bytes(T, E, k)
+ *                bytes (may be NULL when that is 0)
+ * Bookkeeping the grouped expert contractions need; not on the pages.
+ * Bit-exact and deterministic.  A pair whose id is outside [0, E) is
+ * dropped: it is not counted, its pair_to_row entry is -1 and offsets[E]
+ * then falls short of T*k.
+ */
+int moe_permute(const int32_t* topk_ids, int T, int E, int k,
+                int32_t* counts, int32_t* offsets, int32_t* sorted_pairs,
+                int32_t* pair_to_row, void* workspace, size_t workspace_bytes,
+                void* stream);
+
+/*
+ * moe_mxfp4_gate_up_swiglu — first half of every chosen expert's FFN.
+ *   x_bf16       [T, H] bf16 activations, read
+ *   sorted_pairs [T*k], offsets [E+1] from moe_permute, read
+ *   w13_codes    [E, 2I, H/2] uint8, w13_scales [E, 2I, H/32] uint8: per
+ *                expert, rows 0..I-1 are the gate projection, rows I..2I-1
+ *                the up projection (reading), MX blocks along H
+ *   h_bf16       [T*k, I] bf16, written in sorted order: row r belongs to
+ *                pair sorted_pairs[r] and its expert's segment
+ * For row r of expert e with token t = sorted_pairs[r] / k:
+ *   g = W_gate,e x_t, u = W_up,e x_t (fp32 accumulation),
+ *   h_r = bf16_rne(silu(g) * u), silu(g) = g / (1 + exp(-g)).
+ * The SwiGLU form without biases is the reading of the expert FFN (the pages
+ * say only that the experts are MXFP4 and the activations higher precision).
+ * Scale bytes must lie in 0..254; byte 0 (2^-127) is taken as zero, a
+ * difference of at most 6*2^-127 per weight.
+ */
+int moe_mxfp4_gate_up_swiglu(const uint16_t* x_bf16, const int32_t* sorted_pairs,
+                             const int32_t* offsets, int T, int H, int I, int E,
+                             int k, const uint8_t* w13_codes,
+                             const uint8_t* w13_scales, uint16_t* h_bf16,
+                             void* stream);
+
+/*
+ * moe_mxfp4_down — second half of every chosen expert's FFN.
+ *   h_bf16     [T*k, I] bf16 from moe_mxfp4_gate_up_swiglu, read
+ *   offsets    [E+1] from moe_permute, read
+ *   w2_codes   [E, H, I/2] uint8, w2_scales [E, H, I/32] uint8, blocks along I
+ *   y          [T*k, H] f32, written in sorted order: y_r = W_down,e h_r
+ */
+int moe_mxfp4_down(const uint16_t* h_bf16, const int32_t* offsets, int T, int H,
+                   int I, int E, int k, const uint8_t* w2_codes,
+                   const uint8_t* w2_scales, float* y, void* stream);
+
+/*
+ * moe_combine — mix each token's k expert outputs.
+ *   y           [T*k, H] f32 from moe_mxfp4_down, read
+ *   topk_w      [T, k] f32 from moe_route_topk, read
+ *   pair_to_row [T*k] from moe_permute, read
+ *   out         [T, H] f32, written: out_t = sum_{j=0..k-1} w_tj * y[row(t,j)],
+ *               summed in slot order j (deterministic); a dropped pair
+ *               (pair_to_row < 0) contributes nothing
+ */
+int moe_combine(const float* y, const float* topk_w, const int32_t* pair_to_row,
+                int T, int H, int k, float* out, void* stream);
+
+/*
+ * moe_mxfp4_layer — the whole layer: enqueues exactly moe_route_topk,
+ * moe_permute, moe_mxfp4_gate_up_swiglu, moe_mxfp4_down and moe_combine on
+ * `stream`, with the caller's intermediate buffers (topk_ids [T,k],
+ * topk_w [T,k], counts [E], offsets [E+1], sorted_pairs [T*k],
+ * pair_to_row [T*k], h [T*k, I] bf16, y [T*k, H] f32).
+ */
+int moe_mxfp4_layer(const uint16_t* x_bf16, const float* logits, int T, int H,
+                    int I, int E, int k, const uint8_t* w13_codes,
+                    const uint8_t* w13_scales, const uint8_t* w2_codes,
+                    const uint8_t* w2_scales, int32_t* topk_ids, float* topk_w,
+                    int32_t* counts, int32_t* offsets, int32_t* sorted_pairs,
+                    int32_t* pair_to_row, uint16_t* h_bf16, float* y, float* out,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXFP4MOE_H */

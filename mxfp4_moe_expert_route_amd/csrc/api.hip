@@ -1,0 +1,180 @@
+// C ABI of libmxfp4moe: host-side argument checks, then kernel launches.
+// Every check runs before anything is enqueued, and none of them touches the
+// HIP runtime, so invalid calls return an error without a device.
+#include "../../include/mxfp4moe.h"
+#include "common.hpp"
+
+namespace {
+
+constexpr int kMaxE = 1024;
+constexpr int kMaxK = 32;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int launched(hipError_t e) { return e == hipSuccess ? MXM_OK : MXM_ERR_LAUNCH; }
+
+// Shared checks of the routing shape.
+int check_route_shape(int T, int E, int k) {
+  if (T < 0 || E < 1 || E > kMaxE || k < 1 || k > kMaxK || k > E) return MXM_ERR_SHAPE;
+  if (int64_t(T) * k > INT32_MAX) return MXM_ERR_SHAPE;
+  return MXM_OK;
+}
+
+int check_ffn_shape(int T, int H, int I, int E, int k) {
+  const int st = check_route_shape(T, E, k);
+  if (st != MXM_OK) return st;
+  if (H < 32 || I < 32 || H % 32 || I % 32) return MXM_ERR_SHAPE;
+  // weight element counts per expert must fit the kernels' size_t math and the
+  // activation rows their int32 row indices
+  if (int64_t(T) * k * int64_t(H > I ? H : I) > (int64_t(1) << 40)) return MXM_ERR_SHAPE;
+  return MXM_OK;
+}
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+int mxm_version(void) { return 100; }
+
+const char* mxm_status_string(int status) {
+  switch (status) {
+    case MXM_OK: return "MXM_OK";
+    case MXM_ERR_NULL: return "MXM_ERR_NULL: a required pointer is NULL";
+    case MXM_ERR_SHAPE: return "MXM_ERR_SHAPE: a size is out of range";
+    case MXM_ERR_DTYPE: return "MXM_ERR_DTYPE: unknown dtype code";
+    case MXM_ERR_ALIGN: return "MXM_ERR_ALIGN: a pointer is misaligned";
+    case MXM_ERR_LAUNCH: return "MXM_ERR_LAUNCH: a HIP kernel launch failed";
+    case MXM_ERR_UNIMPLEMENTED: return "MXM_ERR_UNIMPLEMENTED";
+    case MXM_ERR_WORKSPACE: return "MXM_ERR_WORKSPACE: workspace too small";
+    default: return "unknown mxfp4moe status";
+  }
+}
+
+int mxfp4_pack(const void* x, int x_dtype, int64_t rows, int64_t K, uint8_t* codes,
+               uint8_t* scales, void* stream) {
+  if (x_dtype != MXM_F32 && x_dtype != MXM_BF16) return MXM_ERR_DTYPE;
+  if (rows < 0 || K < 0 || K % 32) return MXM_ERR_SHAPE;
+  if (rows == 0 || K == 0) return MXM_OK;
+  if (!x || !codes || !scales) return MXM_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(codes, 16)) return MXM_ERR_ALIGN;
+  return launched(mxm::launch_pack(x, x_dtype, rows, K, codes, scales, as_stream(stream)));
+}
+
+int mxfp4_unpack(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t K, void* y,
+                 int y_dtype, void* stream) {
+  if (y_dtype != MXM_F32 && y_dtype != MXM_BF16) return MXM_ERR_DTYPE;
+  if (rows < 0 || K < 0 || K % 32) return MXM_ERR_SHAPE;
+  if (rows == 0 || K == 0) return MXM_OK;
+  if (!codes || !scales || !y) return MXM_ERR_NULL;
+  if (!aligned(codes, 16) || !aligned(y, 16)) return MXM_ERR_ALIGN;
+  return launched(mxm::launch_unpack(codes, scales, rows, K, y, y_dtype, as_stream(stream)));
+}
+
+int moe_route_topk(const float* logits, int T, int E, int k, int32_t* topk_ids, float* topk_w,
+                   void* stream) {
+  const int st = check_route_shape(T, E, k);
+  if (st != MXM_OK) return st;
+  if (T == 0) return MXM_OK;
+  if (!logits || !topk_ids || !topk_w) return MXM_ERR_NULL;
+  if (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4)) return MXM_ERR_ALIGN;
+  return launched(mxm::launch_route_topk(logits, T, E, k, topk_ids, topk_w, as_stream(stream)));
+}
+
+size_t moe_permute_workspace_bytes(int T, int E, int k) {
+  (void)T;
+  (void)E;
+  (void)k;
+  return 0;
+}
+
+int moe_permute(const int32_t* topk_ids, int T, int E, int k, int32_t* counts, int32_t* offsets,
+                int32_t* sorted_pairs, int32_t* pair_to_row, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  const int st = check_route_shape(T, E, k);
+  if (st != MXM_OK) return st;
+  if (workspace_bytes < moe_permute_workspace_bytes(T, E, k)) return MXM_ERR_WORKSPACE;
+  (void)workspace;
+  if (T == 0) return MXM_OK;
+  if (!topk_ids || !counts || !offsets || !sorted_pairs || !pair_to_row) return MXM_ERR_NULL;
+  if (!aligned(topk_ids, 4) || !aligned(counts, 4) || !aligned(offsets, 4) ||
+      !aligned(sorted_pairs, 4) || !aligned(pair_to_row, 4))
+    return MXM_ERR_ALIGN;
+  return launched(mxm::launch_permute(topk_ids, T, E, k, counts, offsets, sorted_pairs,
+                                      pair_to_row, as_stream(stream)));
+}
+
+int moe_mxfp4_gate_up_swiglu(const uint16_t* x_bf16, const int32_t* sorted_pairs,
+                             const int32_t* offsets, int T, int H, int I, int E, int k,
+                             const uint8_t* w13_codes, const uint8_t* w13_scales,
+                             uint16_t* h_bf16, void* stream) {
+  const int st = check_ffn_shape(T, H, I, E, k);
+  if (st != MXM_OK) return st;
+  if (T == 0) return MXM_OK;
+  if (!x_bf16 || !sorted_pairs || !offsets || !w13_codes || !w13_scales || !h_bf16)
+    return MXM_ERR_NULL;
+  if (!aligned(x_bf16, 16) || !aligned(w13_codes, 16) || !aligned(h_bf16, 8) ||
+      !aligned(sorted_pairs, 4) || !aligned(offsets, 4))
+    return MXM_ERR_ALIGN;
+  return launched(mxm::launch_gate_up(x_bf16, sorted_pairs, offsets, T, H, I, E, k, w13_codes,
+                                      w13_scales, h_bf16, as_stream(stream)));
+}
+
+int moe_mxfp4_down(const uint16_t* h_bf16, const int32_t* offsets, int T, int H, int I, int E,
+                   int k, const uint8_t* w2_codes, const uint8_t* w2_scales, float* y,
+                   void* stream) {
+  const int st = check_ffn_shape(T, H, I, E, k);
+  if (st != MXM_OK) return st;
+  if (T == 0) return MXM_OK;
+  if (!h_bf16 || !offsets || !w2_codes || !w2_scales || !y) return MXM_ERR_NULL;
+  if (!aligned(h_bf16, 16) || !aligned(w2_codes, 16) || !aligned(y, 16) || !aligned(offsets, 4))
+    return MXM_ERR_ALIGN;
+  return launched(mxm::launch_down(h_bf16, offsets, T, H, I, E, k, w2_codes, w2_scales, y,
+                                   as_stream(stream)));
+}
+
+int moe_combine(const float* y, const float* topk_w, const int32_t* pair_to_row, int T, int H,
+                int k, float* out, void* stream) {
+  if (T < 0 || k < 1 || k > kMaxK || H < 32 || H % 32) return MXM_ERR_SHAPE;
+  if (int64_t(T) * k > INT32_MAX) return MXM_ERR_SHAPE;
+  if (T == 0) return MXM_OK;
+  if (!y || !topk_w || !pair_to_row || !out) return MXM_ERR_NULL;
+  if (!aligned(y, 16) || !aligned(out, 16) || !aligned(topk_w, 4) || !aligned(pair_to_row, 4))
+    return MXM_ERR_ALIGN;
+  return launched(mxm::launch_combine(y, topk_w, pair_to_row, T, H, k, out, as_stream(stream)));
+}
+
+int moe_mxfp4_layer(const uint16_t* x_bf16, const float* logits, int T, int H, int I, int E,
+                    int k, const uint8_t* w13_codes, const uint8_t* w13_scales,
+                    const uint8_t* w2_codes, const uint8_t* w2_scales, int32_t* topk_ids,
+                    float* topk_w, int32_t* counts, int32_t* offsets, int32_t* sorted_pairs,
+                    int32_t* pair_to_row, uint16_t* h_bf16, float* y, float* out,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  // check everything before enqueuing anything
+  int st = check_ffn_shape(T, H, I, E, k);
+  if (st != MXM_OK) return st;
+  if (workspace_bytes < moe_permute_workspace_bytes(T, E, k)) return MXM_ERR_WORKSPACE;
+  if (T == 0) return MXM_OK;
+  if (!x_bf16 || !logits || !w13_codes || !w13_scales || !w2_codes || !w2_scales || !topk_ids ||
+      !topk_w || !counts || !offsets || !sorted_pairs || !pair_to_row || !h_bf16 || !y || !out)
+    return MXM_ERR_NULL;
+  if (!aligned(x_bf16, 16) || !aligned(w13_codes, 16) || !aligned(w2_codes, 16) ||
+      !aligned(h_bf16, 16) || !aligned(y, 16) || !aligned(out, 16) || !aligned(logits, 4) ||
+      !aligned(topk_ids, 4) || !aligned(topk_w, 4) || !aligned(counts, 4) ||
+      !aligned(offsets, 4) || !aligned(sorted_pairs, 4) || !aligned(pair_to_row, 4))
+    return MXM_ERR_ALIGN;
+  if ((st = moe_route_topk(logits, T, E, k, topk_ids, topk_w, stream)) != MXM_OK) return st;
+  if ((st = moe_permute(topk_ids, T, E, k, counts, offsets, sorted_pairs, pair_to_row, workspace,
+                        workspace_bytes, stream)) != MXM_OK)
+    return st;
+  if ((st = moe_mxfp4_gate_up_swiglu(x_bf16, sorted_pairs, offsets, T, H, I, E, k, w13_codes,
+                                     w13_scales, h_bf16, stream)) != MXM_OK)
+    return st;
+  if ((st = moe_mxfp4_down(h_bf16, offsets, T, H, I, E, k, w2_codes, w2_scales, y, stream)) !=
+      MXM_OK)
+    return st;
+  return moe_combine(y, topk_w, pair_to_row, T, H, k, out, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,119 @@
+// Shared device helpers and the internal launcher interface of libmxfp4moe.
+// gfx950 (CDNA4) only: wave64, MFMA, scaled FP4 conversions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxm {
+
+constexpr int kWave = 64;
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// fp32 -> bf16 bits, round to nearest even; NaN -> canonical quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// E8M0 scale byte -> fp32 2^(e-127) for e in 1..254 (exact normal float).
+// e == 0 gives +0.0f: 2^-127 is below the normal fp32 range; a block with
+// scale byte 0 contributes at most 6 * 2^-127 per weight.
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e) { return __uint_as_float(e << 23); }
+
+// Eight E2M1 codes of one dword (element 2b in the low nibble of byte b)
+// times `scale`, converted to eight bf16 in element order.
+__device__ __forceinline__ bf16x8 dequant8(uint32_t codes, float scale) {
+  bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 0);
+  bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 1);
+  bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 2);
+  bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3);
+  bf16x8 r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Inclusive prefix sum across the 64 lanes of a wave (all lanes active).
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    int o = __shfl_up(v, d);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+// Tile of one expert's row segment: `rows` sorted rows starting at `row0`.
+struct Tile {
+  int e;
+  int row0;
+  int rows;
+};
+
+// Map tile index `tau` to (expert, row range) when every expert's segment of
+// `offsets` is cut into tiles of `mt` rows, experts in order.  Executed by a
+// whole wave (uniform control flow); returns false when tau is past the last
+// tile.  Reads offsets[0..E].
+__device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, int E, int mt,
+                                          int tau, Tile& t) {
+  const int lane = lane_id();
+  int base = 0;
+  for (int c0 = 0; c0 < E; c0 += kWave) {
+    const int e = c0 + lane;
+    int off = 0, cnt = 0;
+    if (e < E) {
+      off = offsets[e];
+      cnt = offsets[e + 1] - off;
+    }
+    const int nt = (cnt + mt - 1) / mt;
+    const int incl = wave_incl_scan(nt);
+    const int total = __shfl(incl, kWave - 1);
+    if (tau < base + total) {
+      const int excl = base + incl - nt;
+      const unsigned long long m = __ballot(tau >= excl && tau < excl + nt);
+      const int src = __ffsll((long long)m) - 1;
+      const int ti = tau - __shfl(excl, src);
+      t.e = c0 + src;
+      t.row0 = __shfl(off, src) + ti * mt;
+      t.rows = min(mt, __shfl(cnt, src) - ti * mt);
+      return true;
+    }
+    base += total;
+  }
+  return false;
+}
+
+// ---------------------------------------------------------------------------
+// internal launchers (defined in the kernel files, called by api.hip after
+// host-side argument checks).  Each returns the hipError_t of its launch.
+
+hipError_t launch_pack(const void* x, int x_dtype, int64_t rows, int64_t K, uint8_t* codes,
+                       uint8_t* scales, hipStream_t s);
+hipError_t launch_unpack(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t K,
+                         void* y, int y_dtype, hipStream_t s);
+hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
+                             hipStream_t s);
+hipError_t launch_permute(const int32_t* ids, int T, int E, int k, int32_t* counts,
+                          int32_t* offsets, int32_t* sorted_pairs, int32_t* pair_to_row,
+                          hipStream_t s);
+hipError_t launch_gate_up(const uint16_t* x, const int32_t* sorted_pairs, const int32_t* offsets,
+                          int T, int H, int I, int E, int k, const uint8_t* codes,
+                          const uint8_t* scales, uint16_t* h, hipStream_t s);
+hipError_t launch_down(const uint16_t* h, const int32_t* offsets, int T, int H, int I, int E,
+                       int k, const uint8_t* codes, const uint8_t* scales, float* y,
+                       hipStream_t s);
+hipError_t launch_combine(const float* y, const float* w, const int32_t* pair_to_row, int T,
+                          int H, int k, float* out, hipStream_t s);
+
+}  // namespace mxm

@@ -103,8 +103,10 @@ def unpack(codes, scales):
 # rounding of float64 values to the storage types
 
 def to_f32(v):
-    """float64 -> float32 with round-to-nearest-even (IEEE conversion)."""
-    return np.asarray(v, dtype=np.float64).astype(np.float32)
+    """float64 -> float32 with round-to-nearest-even (IEEE conversion;
+    magnitudes beyond fp32's range become Inf)."""
+    with np.errstate(over="ignore"):
+        return np.asarray(v, dtype=np.float64).astype(np.float32)
 
 
 def to_bf16_bits(v):

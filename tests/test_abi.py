@@ -1,0 +1,104 @@
+"""The C ABI without a GPU: the library loads, exports every declared entry
+point, and rejects bad arguments on the host before touching the device."""
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "mxfp4moe.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\**\s*([a-z_0-9]+)\s*\(",
+                                 src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from mxfp4_moe_expert_route_amd import _lib
+    assert os.path.exists(_lib.LIB_PATH), "library not built: run __graft_entry__.build()"
+    return _lib.lib()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("mxfp4_pack", "mxfp4_unpack", "moe_route_topk", "moe_permute",
+              "moe_permute_workspace_bytes", "moe_mxfp4_gate_up_swiglu", "moe_mxfp4_down",
+              "moe_combine", "moe_mxfp4_layer", "mxm_status_string", "mxm_version"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported_and_bound(lib):
+    from mxfp4_moe_expert_route_amd import _lib
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+        assert n in _lib.SIGNATURES, n
+
+
+def test_status_strings(lib):
+    for s in range(-7, 1):
+        assert lib.mxm_status_string(s)
+    assert lib.mxm_version() >= 100
+
+
+P = 256        # an aligned fake device address: never dereferenced on error paths
+
+
+def test_pack_unpack_argument_checks(lib):
+    assert lib.mxfp4_pack(P, 7, 4, 64, P, P, None) == -3            # dtype
+    assert lib.mxfp4_pack(P, 0, 4, 48, P, P, None) == -2            # K % 32
+    assert lib.mxfp4_pack(P, 0, -1, 64, P, P, None) == -2
+    assert lib.mxfp4_pack(None, 0, 4, 64, P, P, None) == -1         # null
+    assert lib.mxfp4_pack(P + 4, 0, 4, 64, P, P, None) == -4        # misaligned x
+    assert lib.mxfp4_pack(None, 0, 0, 64, None, None, None) == 0    # empty: no-op
+    assert lib.mxfp4_unpack(P, P, 4, 64, P, 9, None) == -3
+    assert lib.mxfp4_unpack(P, P, 4, 33, P, 0, None) == -2
+    assert lib.mxfp4_unpack(P, None, 4, 64, P, 0, None) == -1
+    assert lib.mxfp4_unpack(P + 8, P, 4, 64, P, 0, None) == -4
+
+
+def test_route_permute_argument_checks(lib):
+    assert lib.moe_route_topk(P, 4, 8, 9, P, P, None) == -2          # k > E
+    assert lib.moe_route_topk(P, 4, 1025, 8, P, P, None) == -2       # E > 1024
+    assert lib.moe_route_topk(P, 4, 64, 33, P, P, None) == -2        # k > 32
+    assert lib.moe_route_topk(P, 4, 8, 0, P, P, None) == -2
+    assert lib.moe_route_topk(None, 4, 8, 2, P, P, None) == -1
+    assert lib.moe_route_topk(P + 2, 4, 8, 2, P, P, None) == -4
+    assert lib.moe_route_topk(None, 0, 8, 2, None, None, None) == 0
+    assert lib.moe_permute_workspace_bytes(64, 384, 8) == 0
+    assert lib.moe_permute(P, 4, 8, 2, P, P, P, None, None, 0, None) == -1
+    assert lib.moe_permute(P, 4, 8, 9, P, P, P, P, None, 0, None) == -2
+
+
+def test_ffn_combine_argument_checks(lib):
+    gu = lib.moe_mxfp4_gate_up_swiglu
+    assert gu(P, P, P, 8, 6160, 2048, 384, 8, P, P, P, None) == -2   # H % 32
+    assert gu(P, P, P, 8, 6144, 2040, 384, 8, P, P, P, None) == -2   # I % 32
+    assert gu(P, P, P, 8, 6144, 2048, 384, 400, P, P, P, None) == -2
+    assert gu(P, None, P, 8, 6144, 2048, 384, 8, P, P, P, None) == -1
+    assert gu(P + 8, P, P, 8, 6144, 2048, 384, 8, P, P, P, None) == -4
+    assert gu(None, None, None, 0, 6144, 2048, 384, 8, None, None, None, None) == 0
+    dn = lib.moe_mxfp4_down
+    assert dn(P, P, 8, 6144, 2048, 384, 8, P, P, None, None) == -1
+    assert dn(P, P, 8, 6144, 16, 384, 8, P, P, P, None) == -2
+    assert dn(P, P, 8, 6144, 2048, 384, 8, P + 4, P, P, None) == -4
+    cb = lib.moe_combine
+    assert cb(P, P, P, 8, 6144, 0, P, None) == -2
+    assert cb(P, P, None, 8, 6144, 8, P, None) == -1
+    assert cb(P, P, P, 8, 6144, 8, P + 4, None) == -4
+    assert cb(None, None, None, 0, 6144, 8, None, None) == 0
+
+
+def test_python_wrappers_reject_host_tensors():
+    import mxfp4_moe_expert_route_amd as mm
+    with pytest.raises(ValueError):
+        mm.mxfp4_pack(torch.zeros(4, 64))
+    with pytest.raises(TypeError):
+        mm.moe_route_topk(torch.zeros(4, 8, dtype=torch.float64), 2)

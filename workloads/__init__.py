@@ -43,6 +43,11 @@ class LayerConfig:
     routing: str = "uniform"     # "uniform" | "zipf"
     zipf_s: float = 1.1
     router_std: float = 0.02
+    layer_id: int = -1           # seeds weights and router; -1: same as cfg_id
+
+    @property
+    def lid(self):
+        return self.cfg_id if self.layer_id < 0 else self.layer_id
 
     @property
     def R(self):
@@ -59,17 +64,17 @@ class LayerConfig:
 
 CONFIGS = {
     # hidden 256, 8 experts, top-2, intermediate 128, 16 tokens; seed 0
-    "tiny_t16": LayerConfig("tiny_t16", 0, 16, 256, 128, 8, 2, 119, 123),
-    # page-shaped layer, one sequence's 8-token verify block
-    "verify_t8": LayerConfig("verify_t8", 1, 8, 6144, 2048, 384, 8, 118, 124),
-    # 8 sequences x 8-token blocks
-    "verify_t64": LayerConfig("verify_t64", 2, 64, 6144, 2048, 384, 8, 118, 124),
-    # 64 sequences x 8 tokens, Zipf(1.1) expert popularity
+    "tiny_t16": LayerConfig("tiny_t16", 0, 16, 256, 128, 8, 2, 119, 123, layer_id=0),
+    # page-shaped layer (layer id 1), one sequence's 8-token verify block
+    "verify_t8": LayerConfig("verify_t8", 1, 8, 6144, 2048, 384, 8, 118, 124, layer_id=1),
+    # same layer, 8 sequences x 8-token blocks
+    "verify_t64": LayerConfig("verify_t64", 2, 64, 6144, 2048, 384, 8, 118, 124, layer_id=1),
+    # same layer, 64 sequences x 8 tokens, Zipf(1.1) expert popularity
     "zipf_t512": LayerConfig("zipf_t512", 3, 512, 6144, 2048, 384, 8, 118, 124,
-                             routing="zipf"),
-    # prefill-like: 8192 tokens, dense expert GEMMs
+                             routing="zipf", layer_id=1),
+    # same layer, prefill-like: 8192 tokens, dense expert GEMMs
     "prefill_t8192": LayerConfig("prefill_t8192", 4, 8192, 6144, 2048, 384, 8,
-                                 118, 124),
+                                 118, 124, layer_id=1),
 }
 
 
@@ -108,7 +113,7 @@ def gen_x_bits(cfg, seed=0):
 
 
 def gen_router(cfg, seed=0):
-    r = _rng(seed, cfg.cfg_id, _T_ROUTER)
+    r = _rng(seed, cfg.lid, _T_ROUTER)
     return r.normal(0.0, cfg.router_std, size=(cfg.E, cfg.H)).astype(np.float32)
 
 
@@ -135,11 +140,11 @@ def expert_weights(cfg, e, seed=0):
     """(w13_codes [2I,H/2], w13_scales [2I,H/32], w2_codes [H,I/2], w2_scales [H,I/32])
     for expert e, all uint8."""
     H, I = cfg.H, cfg.I
-    c13 = _random_bytes(_rng(seed, cfg.cfg_id, _T_W13C, e), 2 * I * H // 2)
-    s13 = _rng(seed, cfg.cfg_id, _T_W13S, e).integers(
+    c13 = _random_bytes(_rng(seed, cfg.lid, _T_W13C, e), 2 * I * H // 2)
+    s13 = _rng(seed, cfg.lid, _T_W13S, e).integers(
         cfg.exp_lo, cfg.exp_hi + 1, size=2 * I * H // 32, dtype=np.uint8)
-    c2 = _random_bytes(_rng(seed, cfg.cfg_id, _T_W2C, e), H * I // 2)
-    s2 = _rng(seed, cfg.cfg_id, _T_W2S, e).integers(
+    c2 = _random_bytes(_rng(seed, cfg.lid, _T_W2C, e), H * I // 2)
+    s2 = _rng(seed, cfg.lid, _T_W2S, e).integers(
         cfg.exp_lo, cfg.exp_hi + 1, size=H * I // 32, dtype=np.uint8)
     return (c13.reshape(2 * I, H // 2), s13.reshape(2 * I, H // 32),
             c2.reshape(H, I // 2), s2.reshape(H, I // 32))
@@ -177,7 +182,8 @@ class LazyExperts:
     _cache = {}
 
     def __getitem__(self, e):
-        key = (self.cfg, self.seed, int(e))
+        key = (self.cfg.lid, self.cfg.H, self.cfg.I, self.cfg.exp_lo, self.cfg.exp_hi, self.seed,
+               int(e))
         if key not in LazyExperts._cache:
             LazyExperts._cache.clear()             # keep one expert resident
             LazyExperts._cache[key] = expert_weights(self.cfg, int(e), self.seed)
