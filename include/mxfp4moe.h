@@ -32,9 +32,10 @@
  *   - An empty problem (T == 0, rows == 0) is a no-op that returns MXM_OK;
  *     its pointers may then be NULL.
  *   - Integer indices are int32 (T*k < 2^31).  H and I must be multiples of
- *     32 (no partial MX blocks).  1 <= k <= min(E, 32), E <= 1024.
- *   - Pointer alignment: codes, x (pack input), y (unpack output), x_bf16,
- *     h_bf16, y and out 16 bytes; everything else 4 bytes.
+ *     32 (no partial MX blocks); the expert contractions take H <= 16384 and
+ *     I <= 8192.  1 <= k <= min(E, 32), E <= 1024.
+ *   - Pointer alignment: codes, expert-weight scales, x (pack input), y
+ *     (unpack output), x_bf16, h_bf16, y and out 16 bytes; everything else 4.
  *     Rows are densely packed (the leading stride is the row length).
  */
 #ifndef MXFP4MOE_H

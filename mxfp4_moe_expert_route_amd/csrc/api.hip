@@ -8,6 +8,8 @@ namespace {
 
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 32;
+constexpr int kMaxH = 16384;
+constexpr int kMaxI = 8192;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -24,6 +26,8 @@ int check_ffn_shape(int T, int H, int I, int E, int k) {
   const int st = check_route_shape(T, E, k);
   if (st != MXM_OK) return st;
   if (H < 32 || I < 32 || H % 32 || I % 32) return MXM_ERR_SHAPE;
+  // per-wave scale staging in LDS must fit a workgroup's 64 KB
+  if (H > kMaxH || I > kMaxI) return MXM_ERR_SHAPE;
   // weight element counts per expert must fit the kernels' size_t math and the
   // activation rows their int32 row indices
   if (int64_t(T) * k * int64_t(H > I ? H : I) > (int64_t(1) << 40)) return MXM_ERR_SHAPE;
@@ -114,8 +118,8 @@ int moe_mxfp4_gate_up_swiglu(const uint16_t* x_bf16, const int32_t* sorted_pairs
   if (T == 0) return MXM_OK;
   if (!x_bf16 || !sorted_pairs || !offsets || !w13_codes || !w13_scales || !h_bf16)
     return MXM_ERR_NULL;
-  if (!aligned(x_bf16, 16) || !aligned(w13_codes, 16) || !aligned(h_bf16, 8) ||
-      !aligned(sorted_pairs, 4) || !aligned(offsets, 4))
+  if (!aligned(x_bf16, 16) || !aligned(w13_codes, 16) || !aligned(w13_scales, 16) ||
+      !aligned(h_bf16, 8) || !aligned(sorted_pairs, 4) || !aligned(offsets, 4))
     return MXM_ERR_ALIGN;
   return launched(mxm::launch_gate_up(x_bf16, sorted_pairs, offsets, T, H, I, E, k, w13_codes,
                                       w13_scales, h_bf16, as_stream(stream)));
@@ -128,7 +132,8 @@ int moe_mxfp4_down(const uint16_t* h_bf16, const int32_t* offsets, int T, int H,
   if (st != MXM_OK) return st;
   if (T == 0) return MXM_OK;
   if (!h_bf16 || !offsets || !w2_codes || !w2_scales || !y) return MXM_ERR_NULL;
-  if (!aligned(h_bf16, 16) || !aligned(w2_codes, 16) || !aligned(y, 16) || !aligned(offsets, 4))
+  if (!aligned(h_bf16, 16) || !aligned(w2_codes, 16) || !aligned(w2_scales, 16) ||
+      !aligned(y, 16) || !aligned(offsets, 4))
     return MXM_ERR_ALIGN;
   return launched(mxm::launch_down(h_bf16, offsets, T, H, I, E, k, w2_codes, w2_scales, y,
                                    as_stream(stream)));
@@ -160,7 +165,7 @@ int moe_mxfp4_layer(const uint16_t* x_bf16, const float* logits, int T, int H, i
       !topk_w || !counts || !offsets || !sorted_pairs || !pair_to_row || !h_bf16 || !y || !out)
     return MXM_ERR_NULL;
   if (!aligned(x_bf16, 16) || !aligned(w13_codes, 16) || !aligned(w2_codes, 16) ||
-      !aligned(h_bf16, 16) || !aligned(y, 16) || !aligned(out, 16) || !aligned(logits, 4) ||
+      !aligned(w13_scales, 16) || !aligned(w2_scales, 16) || !aligned(h_bf16, 16) || !aligned(y, 16) || !aligned(out, 16) || !aligned(logits, 4) ||
       !aligned(topk_ids, 4) || !aligned(topk_w, 4) || !aligned(counts, 4) ||
       !aligned(offsets, 4) || !aligned(sorted_pairs, 4) || !aligned(pair_to_row, 4))
     return MXM_ERR_ALIGN;

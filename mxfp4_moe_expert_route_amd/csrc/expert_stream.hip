@@ -35,42 +35,53 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
 
+// Tunables (compile-time; the defaults are the measured best on MI355X).
+#ifndef MXM_WDEPTH
+#define MXM_WDEPTH 2        // fragments in flight per wave
+#endif
+#ifndef MXM_GU_NSUB
+#define MXM_GU_NSUB 2       // 16-column intermediate subtiles per wave (gate/up)
+#endif
+#ifndef MXM_DN_NSUB
+#define MXM_DN_NSUB 4       // 16-row output subtiles per wave (down)
+#endif
+
+// One step of a lane's streams: one MX block (16 code bytes) of each weight
+// subtile and the 32 matching bf16 activations of each row subtile.
 template <int NA, int MS>
 struct Frag {
-  uint4 c[NA];          // 32 E2M1 codes of this lane's block, per weight subtile
-  uint32_t s[NA];       // the block's E8M0 scale byte
-  uint4 x[MS][4];       // 32 bf16 activations of this lane's block, per row subtile
+  uint4 c[NA];
+  uint4 x[MS][4];
 };
 
+// Loads are unconditional (addresses clamped in bounds) so that no branch
+// separates them: the compiler then keeps MXM_WDEPTH steps in flight instead
+// of draining the load queue before every step.  Rows past the tile's end
+// read a valid row whose output column is never stored.
 template <int NA, int MS>
 __device__ __forceinline__ void load_frag(Frag<NA, MS>& f, const uint8_t* const (&wc)[NA],
-                                          const uint8_t* const (&ws)[NA],
-                                          const uint16_t* const (&xr)[MS], const bool (&xv)[MS],
-                                          int blk, bool ok) {
+                                          const uint16_t* const (&xr)[MS], int blk, int nblk) {
+  const int b = blk < nblk ? blk : nblk - 1;
 #pragma unroll
-  for (int a = 0; a < NA; ++a) {
-    if (ok) {
-      f.c[a] = *reinterpret_cast<const uint4*>(wc[a] + size_t(blk) * 16);
-      f.s[a] = ws[a][blk];
-    } else {
-      f.c[a] = make_uint4(0u, 0u, 0u, 0u);
-      f.s[a] = 0u;
-    }
-  }
+  for (int a = 0; a < NA; ++a) f.c[a] = *reinterpret_cast<const uint4*>(wc[a] + size_t(b) * 16);
 #pragma unroll
   for (int m = 0; m < MS; ++m) {
-    const uint4* src = reinterpret_cast<const uint4*>(xr[m] + size_t(blk) * 32);
+    const uint4* src = reinterpret_cast<const uint4*>(xr[m] + size_t(b) * 32);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      f.x[m][j] = (ok && xv[m]) ? src[j] : make_uint4(0u, 0u, 0u, 0u);
+    for (int j = 0; j < 4; ++j) f.x[m][j] = src[j];
   }
 }
 
+// `sl[a]` points at this lane's row of subtile a's scales in LDS.  A block
+// past the end of K gets scale 0, so it contributes nothing.
 template <int NA, int MS>
-__device__ __forceinline__ void mma_frag(const Frag<NA, MS>& f, f32x4 (&acc)[NA][MS]) {
+__device__ __forceinline__ void mma_frag(const Frag<NA, MS>& f, const uint8_t* const (&sl)[NA],
+                                         int blk, int nblk, f32x4 (&acc)[NA][MS]) {
+  const bool ok = blk < nblk;
+  const int b = ok ? blk : 0;
 #pragma unroll
   for (int a = 0; a < NA; ++a) {
-    const float sc = e8m0_to_f32(f.s[a]);
+    const float sc = ok ? e8m0_to_f32(sl[a][b]) : 0.f;
     const uint32_t cw[4] = {f.c[a].x, f.c[a].y, f.c[a].z, f.c[a].w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -83,22 +94,42 @@ __device__ __forceinline__ void mma_frag(const Frag<NA, MS>& f, f32x4 (&acc)[NA]
   }
 }
 
-// acc[a][m] += W_a (16 rows x K) . X_m (16 rows x K)^T over all nblk MX blocks.
+// Copy the scales of NA 16-row weight subtiles into this wave's LDS area.
+// Rows of a subtile are consecutive, so its scales are one contiguous run of
+// 16*nblk bytes starting at a multiple of 16*nblk: whole 16-byte loads.
+template <int NA>
+__device__ __forceinline__ void stage_scales(const uint8_t* const (&ws0)[NA], int nblk,
+                                             uint8_t* lds) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int a = 0; a < NA; ++a) {
+    const uint4* src = reinterpret_cast<const uint4*>(ws0[a]);
+    uint4* dst = reinterpret_cast<uint4*>(lds + a * 16 * nblk);
+    for (int i = lane; i < nblk; i += kWave) dst[i] = src[i];
+  }
+}
+
+// acc[a][m] += W_a (16 rows x K) . X_m (16 rows x K)^T over all nblk MX blocks,
+// with MXM_WDEPTH steps of code/activation loads in flight.  The step count is
+// padded to a multiple of the depth with zero-scale steps so the ring of
+// fragments has compile-time indices and the loop body has no branch.
 template <int NA, int MS>
 __device__ __forceinline__ void stream_k(const uint8_t* const (&wc)[NA],
-                                         const uint8_t* const (&ws)[NA],
-                                         const uint16_t* const (&xr)[MS], const bool (&xv)[MS],
-                                         int nblk, f32x4 (&acc)[NA][MS]) {
+                                         const uint8_t* const (&sl)[NA],
+                                         const uint16_t* const (&xr)[MS], int nblk,
+                                         f32x4 (&acc)[NA][MS]) {
+  constexpr int D = MXM_WDEPTH;
   const int g = lane_id() >> 4;
-  const int nsteps = (nblk + 3) >> 2;
-  Frag<NA, MS> cur;
-  load_frag<NA, MS>(cur, wc, ws, xr, xv, g, g < nblk);
-  for (int s = 0; s < nsteps; ++s) {
-    Frag<NA, MS> nxt;
-    const int blk = 4 * (s + 1) + g;
-    if (s + 1 < nsteps) load_frag<NA, MS>(nxt, wc, ws, xr, xv, blk, blk < nblk);
-    mma_frag<NA, MS>(cur, acc);
-    cur = nxt;
+  const int nsteps = (((nblk + 3) >> 2) + D - 1) / D * D;
+  Frag<NA, MS> f[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) load_frag<NA, MS>(f[d], wc, xr, 4 * d + g, nblk);
+  for (int s0 = 0; s0 < nsteps; s0 += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      mma_frag<NA, MS>(f[d], sl, 4 * (s0 + d) + g, nblk, acc);
+      load_frag<NA, MS>(f[d], wc, xr, 4 * (s0 + d + D) + g, nblk);
+    }
   }
 }
 
@@ -126,23 +157,28 @@ __global__ __launch_bounds__(kThreads) void k_gate_up(
   const int i0 = (nt * kWaves + wave) * 16 * NSUB;
   if (i0 >= I) return;
 
+  const int nblk = H / 32;
   const size_t erow = size_t(t.e) * 2 * I;
-  const uint8_t* wc[NA];
-  const uint8_t* ws[NA];
+  const uint8_t* wc[NA];      // this lane's weight row, per subtile
+  const uint8_t* ws0[NA];     // first scale byte of each subtile (16 rows)
+  const uint8_t* sl[NA];      // this lane's scale row in LDS
+  extern __shared__ uint8_t lds_scales[];
+  uint8_t* my_lds = lds_scales + wave * NA * 16 * nblk;
 #pragma unroll
   for (int a = 0; a < NSUB; ++a) {
-    const int col = min(i0 + 16 * a, I - 16) + r16;       // clamp keeps loads in bounds
-    wc[a] = codes + (erow + col) * size_t(H / 2);
-    ws[a] = scales + (erow + col) * size_t(H / 32);
-    wc[NSUB + a] = codes + (erow + I + col) * size_t(H / 2);
-    ws[NSUB + a] = scales + (erow + I + col) * size_t(H / 32);
+    const int c0 = min(i0 + 16 * a, I - 16);             // clamp keeps loads in bounds
+    wc[a] = codes + (erow + c0 + r16) * size_t(H / 2);
+    wc[NSUB + a] = codes + (erow + I + c0 + r16) * size_t(H / 2);
+    ws0[a] = scales + (erow + c0) * size_t(nblk);
+    ws0[NSUB + a] = scales + (erow + I + c0) * size_t(nblk);
   }
-  const uint16_t* xr[MS];
-  bool xv[MS];
+#pragma unroll
+  for (int a = 0; a < NA; ++a) sl[a] = my_lds + a * 16 * nblk + r16 * nblk;
+  stage_scales<NA>(ws0, nblk, my_lds);
+  const uint16_t* xr[MS];          // rows past the tile's end re-read its last row
 #pragma unroll
   for (int m = 0; m < MS; ++m) {
     const int mi = 16 * m + r16;
-    xv[m] = mi < t.rows;
     const int row = t.row0 + min(mi, t.rows - 1);
     xr[m] = x + size_t(sorted_pairs[row] / k) * H;
   }
@@ -152,7 +188,7 @@ __global__ __launch_bounds__(kThreads) void k_gate_up(
 #pragma unroll
     for (int m = 0; m < MS; ++m) acc[a][m] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  stream_k<NA, MS>(wc, ws, xr, xv, H / 32, acc);
+  stream_k<NA, MS>(wc, sl, xr, nblk, acc);
 
   // lane holds D[4g+v][r16]: intermediate column i0+16a+4g+v of row r16
 #pragma unroll
@@ -193,21 +229,25 @@ __global__ __launch_bounds__(kThreads) void k_down(
   const int n0 = (nt * kWaves + wave) * 16 * NSUB;
   if (n0 >= H) return;
 
+  const int nblk = I / 32;
   const size_t erow = size_t(t.e) * H;
   const uint8_t* wc[NSUB];
-  const uint8_t* ws[NSUB];
+  const uint8_t* ws0[NSUB];
+  const uint8_t* sl[NSUB];
+  extern __shared__ uint8_t lds_scales[];
+  uint8_t* my_lds = lds_scales + wave * NSUB * 16 * nblk;
 #pragma unroll
   for (int a = 0; a < NSUB; ++a) {
-    const int n = min(n0 + 16 * a, H - 16) + r16;
-    wc[a] = codes + (erow + n) * size_t(I / 2);
-    ws[a] = scales + (erow + n) * size_t(I / 32);
+    const int n0a = min(n0 + 16 * a, H - 16);
+    wc[a] = codes + (erow + n0a + r16) * size_t(I / 2);
+    ws0[a] = scales + (erow + n0a) * size_t(nblk);
+    sl[a] = my_lds + a * 16 * nblk + r16 * nblk;
   }
-  const uint16_t* xr[MS];
-  bool xv[MS];
+  stage_scales<NSUB>(ws0, nblk, my_lds);
+  const uint16_t* xr[MS];          // rows past the tile's end re-read its last row
 #pragma unroll
   for (int m = 0; m < MS; ++m) {
     const int mi = 16 * m + r16;
-    xv[m] = mi < t.rows;
     xr[m] = hin + size_t(t.row0 + min(mi, t.rows - 1)) * I;
   }
   f32x4 acc[NSUB][MS];
@@ -216,7 +256,7 @@ __global__ __launch_bounds__(kThreads) void k_down(
 #pragma unroll
     for (int m = 0; m < MS; ++m) acc[a][m] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  stream_k<NSUB, MS>(wc, ws, xr, xv, I / 32, acc);
+  stream_k<NSUB, MS>(wc, sl, xr, nblk, acc);
 
 #pragma unroll
   for (int a = 0; a < NSUB; ++a) {
@@ -248,23 +288,25 @@ template <int MS>
 hipError_t gate_up_ms(const uint16_t* x, const int32_t* sp, const int32_t* off, int T, int H,
                       int I, int E, int k, const uint8_t* c, const uint8_t* sc, uint16_t* h,
                       hipStream_t s) {
-  constexpr int NSUB = 1;
+  constexpr int NSUB = MXM_GU_NSUB;
   const int R = T * k;
   const int ntile_n = (I + kWaves * 16 * NSUB - 1) / (kWaves * 16 * NSUB);
   const int64_t grid = int64_t(tile_slots(R, E, 16 * MS)) * ntile_n;
-  k_gate_up<MS, NSUB><<<dim3(unsigned(grid)), kThreads, 0, s>>>(x, sp, off, H, I, E, k, c, sc, h,
-                                                                  ntile_n);
+  const size_t lds = size_t(kWaves) * 2 * NSUB * 16 * (H / 32);
+  k_gate_up<MS, NSUB><<<dim3(unsigned(grid)), kThreads, lds, s>>>(x, sp, off, H, I, E, k, c, sc,
+                                                                    h, ntile_n);
   return hipGetLastError();
 }
 
 template <int MS>
 hipError_t down_ms(const uint16_t* h, const int32_t* off, int T, int H, int I, int E, int k,
                    const uint8_t* c, const uint8_t* sc, float* y, hipStream_t s) {
-  constexpr int NSUB = 4;
+  constexpr int NSUB = MXM_DN_NSUB;
   const int R = T * k;
   const int ntile_n = (H + kWaves * 16 * NSUB - 1) / (kWaves * 16 * NSUB);
   const int64_t grid = int64_t(tile_slots(R, E, 16 * MS)) * ntile_n;
-  k_down<MS, NSUB><<<dim3(unsigned(grid)), kThreads, 0, s>>>(h, off, H, I, E, c, sc, y, ntile_n);
+  const size_t lds = size_t(kWaves) * NSUB * 16 * (I / 32);
+  k_down<MS, NSUB><<<dim3(unsigned(grid)), kThreads, lds, s>>>(h, off, H, I, E, c, sc, y, ntile_n);
   return hipGetLastError();
 }
 
