@@ -36,6 +36,16 @@ int check_ffn_shape(int T, int H, int I, int E, int k) {
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
+// Experts with many rows go to the LDS-tiled dense kernel, the rest to the
+// streaming kernel.  Chosen from host-known sizes only: the dense pass is
+// worth a launch when the mean rows per touched expert is at least 8 (so
+// some experts may reach its row threshold).
+bool use_dense(int T, int H, int I, int E, int k) {
+  const int64_t R = int64_t(T) * k;
+  const int64_t touched = R < E ? R : E;
+  return mxm::dense_supported(T, H, I, E, k) && R >= 8 * touched;
+}
+
 }  // namespace
 
 extern "C" {
@@ -121,8 +131,16 @@ int moe_mxfp4_gate_up_swiglu(const uint16_t* x_bf16, const int32_t* sorted_pairs
   if (!aligned(x_bf16, 16) || !aligned(w13_codes, 16) || !aligned(w13_scales, 16) ||
       !aligned(h_bf16, 8) || !aligned(sorted_pairs, 4) || !aligned(offsets, 4))
     return MXM_ERR_ALIGN;
+  hipStream_t s = as_stream(stream);
+  int hi = INT32_MAX;
+  if (use_dense(T, H, I, E, k)) {
+    if (mxm::launch_gate_up_dense(x_bf16, sorted_pairs, offsets, T, H, I, E, k, w13_codes,
+                                  w13_scales, h_bf16, s) != hipSuccess)
+      return MXM_ERR_LAUNCH;
+    hi = mxm::dense_min_rows();
+  }
   return launched(mxm::launch_gate_up(x_bf16, sorted_pairs, offsets, T, H, I, E, k, w13_codes,
-                                      w13_scales, h_bf16, as_stream(stream)));
+                                      w13_scales, h_bf16, hi, s));
 }
 
 int moe_mxfp4_down(const uint16_t* h_bf16, const int32_t* offsets, int T, int H, int I, int E,
@@ -135,8 +153,15 @@ int moe_mxfp4_down(const uint16_t* h_bf16, const int32_t* offsets, int T, int H,
   if (!aligned(h_bf16, 16) || !aligned(w2_codes, 16) || !aligned(w2_scales, 16) ||
       !aligned(y, 16) || !aligned(offsets, 4))
     return MXM_ERR_ALIGN;
-  return launched(mxm::launch_down(h_bf16, offsets, T, H, I, E, k, w2_codes, w2_scales, y,
-                                   as_stream(stream)));
+  hipStream_t s = as_stream(stream);
+  int hi = INT32_MAX;
+  if (use_dense(T, H, I, E, k)) {
+    if (mxm::launch_down_dense(h_bf16, offsets, T, H, I, E, k, w2_codes, w2_scales, y, s) !=
+        hipSuccess)
+      return MXM_ERR_LAUNCH;
+    hi = mxm::dense_min_rows();
+  }
+  return launched(mxm::launch_down(h_bf16, offsets, T, H, I, E, k, w2_codes, w2_scales, y, hi, s));
 }
 
 int moe_combine(const float* y, const float* topk_w, const int32_t* pair_to_row, int T, int H,

@@ -62,11 +62,12 @@ struct Tile {
 };
 
 // Map tile index `tau` to (expert, row range) when every expert's segment of
-// `offsets` is cut into tiles of `mt` rows, experts in order.  Executed by a
+// `offsets` is cut into tiles of `mt` rows, experts in order.  Only experts
+// with lo <= rows < hi take part (the others own no tiles).  Executed by a
 // whole wave (uniform control flow); returns false when tau is past the last
 // tile.  Reads offsets[0..E].
 __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, int E, int mt,
-                                          int tau, Tile& t) {
+                                          int tau, Tile& t, int lo = 1, int hi = 0x7fffffff) {
   const int lane = lane_id();
   int base = 0;
   for (int c0 = 0; c0 < E; c0 += kWave) {
@@ -76,6 +77,7 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, i
       off = offsets[e];
       cnt = offsets[e + 1] - off;
     }
+    if (cnt < lo || cnt >= hi) cnt = 0;
     const int nt = (cnt + mt - 1) / mt;
     const int incl = wave_incl_scan(nt);
     const int total = __shfl(incl, kWave - 1);
@@ -107,12 +109,25 @@ hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* 
 hipError_t launch_permute(const int32_t* ids, int T, int E, int k, int32_t* counts,
                           int32_t* offsets, int32_t* sorted_pairs, int32_t* pair_to_row,
                           hipStream_t s);
+// Streaming kernels: experts with fewer than `hi` rows (all when hi is INT_MAX).
 hipError_t launch_gate_up(const uint16_t* x, const int32_t* sorted_pairs, const int32_t* offsets,
                           int T, int H, int I, int E, int k, const uint8_t* codes,
-                          const uint8_t* scales, uint16_t* h, hipStream_t s);
+                          const uint8_t* scales, uint16_t* h, int hi, hipStream_t s);
 hipError_t launch_down(const uint16_t* h, const int32_t* offsets, int T, int H, int I, int E,
-                       int k, const uint8_t* codes, const uint8_t* scales, float* y,
+                       int k, const uint8_t* codes, const uint8_t* scales, float* y, int hi,
                        hipStream_t s);
+
+// Grouped contractions for experts with many rows (LDS-tiled MFMA GEMM).
+// Experts with fewer than `min_rows` rows are left to the streaming kernels.
+bool dense_supported(int T, int H, int I, int E, int k);
+int dense_min_rows();
+hipError_t launch_gate_up_dense(const uint16_t* x, const int32_t* sorted_pairs,
+                                const int32_t* offsets, int T, int H, int I, int E, int k,
+                                const uint8_t* codes, const uint8_t* scales, uint16_t* h,
+                                hipStream_t s);
+hipError_t launch_down_dense(const uint16_t* h, const int32_t* offsets, int T, int H, int I,
+                             int E, int k, const uint8_t* codes, const uint8_t* scales, float* y,
+                             hipStream_t s);
 hipError_t launch_combine(const float* y, const float* w, const int32_t* pair_to_row, int T,
                           int H, int k, float* out, hipStream_t s);
 

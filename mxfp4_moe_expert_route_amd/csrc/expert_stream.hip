@@ -144,7 +144,7 @@ __global__ __launch_bounds__(kThreads) void k_gate_up(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ sorted_pairs,
     const int32_t* __restrict__ offsets, int H, int I, int E, int k,
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
-    uint16_t* __restrict__ h, int ntile_n) {
+    uint16_t* __restrict__ h, int ntile_n, int hi) {
   constexpr int NA = 2 * NSUB;
   const int wave = threadIdx.x >> 6;
   const int lane = lane_id();
@@ -153,7 +153,7 @@ __global__ __launch_bounds__(kThreads) void k_gate_up(
   const int slot = blockIdx.x / ntile_n;
   const int nt = blockIdx.x - slot * ntile_n;
   Tile t;
-  if (!find_tile(offsets, E, 16 * MS, slot, t)) return;
+  if (!find_tile(offsets, E, 16 * MS, slot, t, 1, hi)) return;
   const int i0 = (nt * kWaves + wave) * 16 * NSUB;
   if (i0 >= I) return;
 
@@ -217,7 +217,7 @@ template <int MS, int NSUB>
 __global__ __launch_bounds__(kThreads) void k_down(
     const uint16_t* __restrict__ hin, const int32_t* __restrict__ offsets, int H, int I, int E,
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, float* __restrict__ y,
-    int ntile_n) {
+    int ntile_n, int hi) {
   const int wave = threadIdx.x >> 6;
   const int lane = lane_id();
   const int r16 = lane & 15;
@@ -225,7 +225,7 @@ __global__ __launch_bounds__(kThreads) void k_down(
   const int slot = blockIdx.x / ntile_n;
   const int nt = blockIdx.x - slot * ntile_n;
   Tile t;
-  if (!find_tile(offsets, E, 16 * MS, slot, t)) return;
+  if (!find_tile(offsets, E, 16 * MS, slot, t, 1, hi)) return;
   const int n0 = (nt * kWaves + wave) * 16 * NSUB;
   if (n0 >= H) return;
 
@@ -287,26 +287,27 @@ int tile_slots(int R, int E, int mt) { return (R < E ? R : E) + (R + mt - 1) / m
 template <int MS>
 hipError_t gate_up_ms(const uint16_t* x, const int32_t* sp, const int32_t* off, int T, int H,
                       int I, int E, int k, const uint8_t* c, const uint8_t* sc, uint16_t* h,
-                      hipStream_t s) {
+                      int hi, hipStream_t s) {
   constexpr int NSUB = MXM_GU_NSUB;
   const int R = T * k;
   const int ntile_n = (I + kWaves * 16 * NSUB - 1) / (kWaves * 16 * NSUB);
   const int64_t grid = int64_t(tile_slots(R, E, 16 * MS)) * ntile_n;
   const size_t lds = size_t(kWaves) * 2 * NSUB * 16 * (H / 32);
   k_gate_up<MS, NSUB><<<dim3(unsigned(grid)), kThreads, lds, s>>>(x, sp, off, H, I, E, k, c, sc,
-                                                                    h, ntile_n);
+                                                                    h, ntile_n, hi);
   return hipGetLastError();
 }
 
 template <int MS>
 hipError_t down_ms(const uint16_t* h, const int32_t* off, int T, int H, int I, int E, int k,
-                   const uint8_t* c, const uint8_t* sc, float* y, hipStream_t s) {
+                   const uint8_t* c, const uint8_t* sc, float* y, int hi, hipStream_t s) {
   constexpr int NSUB = MXM_DN_NSUB;
   const int R = T * k;
   const int ntile_n = (H + kWaves * 16 * NSUB - 1) / (kWaves * 16 * NSUB);
   const int64_t grid = int64_t(tile_slots(R, E, 16 * MS)) * ntile_n;
   const size_t lds = size_t(kWaves) * NSUB * 16 * (I / 32);
-  k_down<MS, NSUB><<<dim3(unsigned(grid)), kThreads, lds, s>>>(h, off, H, I, E, c, sc, y, ntile_n);
+  k_down<MS, NSUB><<<dim3(unsigned(grid)), kThreads, lds, s>>>(h, off, H, I, E, c, sc, y, ntile_n,
+                                                               hi);
   return hipGetLastError();
 }
 
@@ -314,21 +315,21 @@ hipError_t down_ms(const uint16_t* h, const int32_t* off, int T, int H, int I, i
 
 hipError_t launch_gate_up(const uint16_t* x, const int32_t* sorted_pairs, const int32_t* offsets,
                           int T, int H, int I, int E, int k, const uint8_t* codes,
-                          const uint8_t* scales, uint16_t* h, hipStream_t s) {
+                          const uint8_t* scales, uint16_t* h, int hi, hipStream_t s) {
   switch (choose_ms(T * k, E)) {
-    case 1: return gate_up_ms<1>(x, sorted_pairs, offsets, T, H, I, E, k, codes, scales, h, s);
-    case 2: return gate_up_ms<2>(x, sorted_pairs, offsets, T, H, I, E, k, codes, scales, h, s);
-    default: return gate_up_ms<4>(x, sorted_pairs, offsets, T, H, I, E, k, codes, scales, h, s);
+    case 1: return gate_up_ms<1>(x, sorted_pairs, offsets, T, H, I, E, k, codes, scales, h, hi, s);
+    case 2: return gate_up_ms<2>(x, sorted_pairs, offsets, T, H, I, E, k, codes, scales, h, hi, s);
+    default: return gate_up_ms<4>(x, sorted_pairs, offsets, T, H, I, E, k, codes, scales, h, hi, s);
   }
 }
 
 hipError_t launch_down(const uint16_t* h, const int32_t* offsets, int T, int H, int I, int E,
-                       int k, const uint8_t* codes, const uint8_t* scales, float* y,
+                       int k, const uint8_t* codes, const uint8_t* scales, float* y, int hi,
                        hipStream_t s) {
   switch (choose_ms(T * k, E)) {
-    case 1: return down_ms<1>(h, offsets, T, H, I, E, k, codes, scales, y, s);
-    case 2: return down_ms<2>(h, offsets, T, H, I, E, k, codes, scales, y, s);
-    default: return down_ms<4>(h, offsets, T, H, I, E, k, codes, scales, y, s);
+    case 1: return down_ms<1>(h, offsets, T, H, I, E, k, codes, scales, y, hi, s);
+    case 2: return down_ms<2>(h, offsets, T, H, I, E, k, codes, scales, y, hi, s);
+    default: return down_ms<4>(h, offsets, T, H, I, E, k, codes, scales, y, hi, s);
   }
 }
 

@@ -30,6 +30,15 @@ SMALL = [
     ("wide_k", (300, 2048, 512, 32, 8)),
 ]
 
+# shapes that take the LDS-tiled dense kernel (H, I multiples of 512, many
+# rows per expert): one tile per expert, several tiles per expert, and a
+# skewed mix where only the popular experts are dense
+DENSE = [
+    ("dense_one_tile", (300, 512, 512, 8, 4), "uniform"),
+    ("dense_two_tiles", (700, 512, 1024, 4, 2), "uniform"),
+    ("dense_mixed_zipf", (256, 1024, 512, 64, 8), "zipf"),
+]
+
 
 @pytest.fixture(scope="module")
 def mm():
@@ -48,6 +57,19 @@ def test_layer_small_every_token(mm, name, shape):
     say("layer", name, cfg)
     d = workloads.layer_inputs(cfg, 0)
     check_layer(cfg, d["x_bits"], d["logits"], d, upload_weights(d))
+
+
+@pytest.mark.parametrize("name,shape,routing", DENSE, ids=[d[0] for d in DENSE])
+def test_layer_dense_path_every_token(mm, name, shape, routing):
+    T, H, I, E, k = shape
+    cfg = workloads.custom_config(name, 700 + [d[0] for d in DENSE].index(name), T, H, I, E, k,
+                                  routing=routing)
+    say("layer", name, cfg)
+    d = workloads.layer_inputs(cfg, 0)
+    b, ref, _ = check_layer(cfg, d["x_bits"], d["logits"], d, upload_weights(d))
+    counts = b.counts.cpu().numpy()
+    say("  rows per expert: min %d max %d" % (counts.min(), counts.max()))
+    assert counts.max() >= 64                        # at least one expert takes the dense kernel
 
 
 def test_layer_is_deterministic(mm):
