@@ -117,6 +117,17 @@ hipError_t launch_down(const uint16_t* h, const int32_t* offsets, int T, int H, 
                        int k, const uint8_t* codes, const uint8_t* scales, float* y, int hi,
                        hipStream_t s);
 
+// Persistent decode-size variant of the streaming kernels (16-row tiles, one
+// workgroup per CU, LDS-staged weight stream).  Same arguments and results.
+bool decode_supported(int T, int H, int I, int E, int k);
+hipError_t launch_gate_up_decode(const uint16_t* x, const int32_t* sorted_pairs,
+                                 const int32_t* offsets, int T, int H, int I, int E, int k,
+                                 const uint8_t* codes, const uint8_t* scales, uint16_t* h, int hi,
+                                 hipStream_t s);
+hipError_t launch_down_decode(const uint16_t* h, const int32_t* offsets, int T, int H, int I,
+                              int E, int k, const uint8_t* codes, const uint8_t* scales, float* y,
+                              int hi, hipStream_t s);
+
 // Grouped contractions for experts with many rows (LDS-tiled MFMA GEMM).
 // Experts with fewer than `min_rows` rows are left to the streaming kernels.
 bool dense_supported(int T, int H, int I, int E, int k);

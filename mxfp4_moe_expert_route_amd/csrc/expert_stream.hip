@@ -94,18 +94,34 @@ __device__ __forceinline__ void mma_frag(const Frag<NA, MS>& f, const uint8_t* c
   }
 }
 
-// Copy the scales of NA 16-row weight subtiles into this wave's LDS area.
-// Rows of a subtile are consecutive, so its scales are one contiguous run of
-// 16*nblk bytes starting at a multiple of 16*nblk: whole 16-byte loads.
+typedef __attribute__((address_space(3))) void lds_void;
+
+// s_waitcnt immediate that waits for vmcnt <= n and nothing else (gfx9 layout:
+// vmcnt low bits 3:0, high bits 15:14; expcnt 6:4 and lgkmcnt 11:8 at max).
+#define MXM_VMCNT(n) ((((n) & 15) | (((n) >> 4) << 14)) | (7 << 4) | (15 << 8))
+
+// One asynchronous 16-byte global->LDS load per lane: lane L writes its 16
+// bytes at lds + 16L.
+__device__ __forceinline__ void dma16(const uint8_t* g, uint8_t* lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 16, 0, 0);
+}
+
+// Start copying the scales of NA 16-row weight subtiles into this wave's LDS
+// area.  Rows of a subtile are consecutive, so its scales are one contiguous
+// run of 16*nblk bytes starting at a multiple of 16*nblk: whole 16-byte
+// chunks, moved by asynchronous global->LDS loads (lane L of an instruction
+// lands at its base + 16L), all issued back to back so the copy costs one
+// memory latency.  The caller waits for vmcnt before reading the area.
 template <int NA>
 __device__ __forceinline__ void stage_scales(const uint8_t* const (&ws0)[NA], int nblk,
                                              uint8_t* lds) {
   const int lane = lane_id();
 #pragma unroll
   for (int a = 0; a < NA; ++a) {
-    const uint4* src = reinterpret_cast<const uint4*>(ws0[a]);
-    uint4* dst = reinterpret_cast<uint4*>(lds + a * 16 * nblk);
-    for (int i = lane; i < nblk; i += kWave) dst[i] = src[i];
+    for (int i0 = 0; i0 < nblk; i0 += kWave) {
+      if (i0 + lane < nblk)
+        dma16(ws0[a] + size_t(i0 + lane) * 16, lds + a * 16 * nblk + i0 * 16);
+    }
   }
 }
 
@@ -115,6 +131,7 @@ __device__ __forceinline__ void stage_scales(const uint8_t* const (&ws0)[NA], in
 // fragments has compile-time indices and the loop body has no branch.
 template <int NA, int MS>
 __device__ __forceinline__ void stream_k(const uint8_t* const (&wc)[NA],
+                                         const uint8_t* const (&ws0)[NA], uint8_t* my_lds,
                                          const uint8_t* const (&sl)[NA],
                                          const uint16_t* const (&xr)[MS], int nblk,
                                          f32x4 (&acc)[NA][MS]) {
@@ -124,7 +141,18 @@ __device__ __forceinline__ void stream_k(const uint8_t* const (&wc)[NA],
   Frag<NA, MS> f[D];
 #pragma unroll
   for (int d = 0; d < D; ++d) load_frag<NA, MS>(f[d], wc, xr, 4 * d + g, nblk);
+  stage_scales<NA>(ws0, nblk, my_lds);
+  // the first fragments and the scale copy land together
+  __builtin_amdgcn_s_waitcnt(MXM_VMCNT(0));
   for (int s0 = 0; s0 < nsteps; s0 += D) {
+#ifdef MXM_PRIO
+    // issue priority falls as the wave progresses, so that the waves of a
+    // SIMD move together instead of oldest-first
+    if (s0 == 0) __builtin_amdgcn_s_setprio(3);
+    else if (s0 == ((nsteps >> 2) & ~(D - 1))) __builtin_amdgcn_s_setprio(2);
+    else if (s0 == ((nsteps >> 1) & ~(D - 1))) __builtin_amdgcn_s_setprio(1);
+    else if (s0 == ((3 * nsteps >> 2) & ~(D - 1))) __builtin_amdgcn_s_setprio(0);
+#endif
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       mma_frag<NA, MS>(f[d], sl, 4 * (s0 + d) + g, nblk, acc);
@@ -174,7 +202,6 @@ __global__ __launch_bounds__(kThreads) void k_gate_up(
   }
 #pragma unroll
   for (int a = 0; a < NA; ++a) sl[a] = my_lds + a * 16 * nblk + r16 * nblk;
-  stage_scales<NA>(ws0, nblk, my_lds);
   const uint16_t* xr[MS];          // rows past the tile's end re-read its last row
 #pragma unroll
   for (int m = 0; m < MS; ++m) {
@@ -188,7 +215,7 @@ __global__ __launch_bounds__(kThreads) void k_gate_up(
 #pragma unroll
     for (int m = 0; m < MS; ++m) acc[a][m] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  stream_k<NA, MS>(wc, sl, xr, nblk, acc);
+  stream_k<NA, MS>(wc, ws0, my_lds, sl, xr, nblk, acc);
 
   // lane holds D[4g+v][r16]: intermediate column i0+16a+4g+v of row r16
 #pragma unroll
@@ -243,7 +270,6 @@ __global__ __launch_bounds__(kThreads) void k_down(
     ws0[a] = scales + (erow + n0a) * size_t(nblk);
     sl[a] = my_lds + a * 16 * nblk + r16 * nblk;
   }
-  stage_scales<NSUB>(ws0, nblk, my_lds);
   const uint16_t* xr[MS];          // rows past the tile's end re-read its last row
 #pragma unroll
   for (int m = 0; m < MS; ++m) {
@@ -256,7 +282,7 @@ __global__ __launch_bounds__(kThreads) void k_down(
 #pragma unroll
     for (int m = 0; m < MS; ++m) acc[a][m] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  stream_k<NSUB, MS>(wc, sl, xr, nblk, acc);
+  stream_k<NSUB, MS>(wc, ws0, my_lds, sl, xr, nblk, acc);
 
 #pragma unroll
   for (int a = 0; a < NSUB; ++a) {
@@ -317,7 +343,13 @@ hipError_t launch_gate_up(const uint16_t* x, const int32_t* sorted_pairs, const 
                           int T, int H, int I, int E, int k, const uint8_t* codes,
                           const uint8_t* scales, uint16_t* h, int hi, hipStream_t s) {
   switch (choose_ms(T * k, E)) {
-    case 1: return gate_up_ms<1>(x, sorted_pairs, offsets, T, H, I, E, k, codes, scales, h, hi, s);
+    case 1:
+#ifndef MXM_NO_DECODE
+      if (decode_supported(T, H, I, E, k))
+        return launch_gate_up_decode(x, sorted_pairs, offsets, T, H, I, E, k, codes, scales, h, hi,
+                                     s);
+#endif
+      return gate_up_ms<1>(x, sorted_pairs, offsets, T, H, I, E, k, codes, scales, h, hi, s);
     case 2: return gate_up_ms<2>(x, sorted_pairs, offsets, T, H, I, E, k, codes, scales, h, hi, s);
     default: return gate_up_ms<4>(x, sorted_pairs, offsets, T, H, I, E, k, codes, scales, h, hi, s);
   }
@@ -327,7 +359,12 @@ hipError_t launch_down(const uint16_t* h, const int32_t* offsets, int T, int H, 
                        int k, const uint8_t* codes, const uint8_t* scales, float* y, int hi,
                        hipStream_t s) {
   switch (choose_ms(T * k, E)) {
-    case 1: return down_ms<1>(h, offsets, T, H, I, E, k, codes, scales, y, hi, s);
+    case 1:
+#ifndef MXM_NO_DECODE
+      if (decode_supported(T, H, I, E, k))
+        return launch_down_decode(h, offsets, T, H, I, E, k, codes, scales, y, hi, s);
+#endif
+      return down_ms<1>(h, offsets, T, H, I, E, k, codes, scales, y, hi, s);
     case 2: return down_ms<2>(h, offsets, T, H, I, E, k, codes, scales, y, hi, s);
     default: return down_ms<4>(h, offsets, T, H, I, E, k, codes, scales, y, hi, s);
   }

@@ -39,6 +39,16 @@ DENSE = [
     ("dense_mixed_zipf", (256, 1024, 512, 64, 8), "zipf"),
 ]
 
+# shapes that take the persistent decode kernel (H, I multiples of 2048, at
+# most 16 rows per expert on average): a single token, experts split into
+# several 16-row tiles by skewed routing, and enough units that each
+# workgroup's run crosses several units and tiles
+DECODE = [
+    ("decode_one_tok", (1, 2048, 2048, 8, 4), "uniform"),
+    ("decode_zipf_tiles", (64, 2048, 2048, 16, 2), "zipf"),
+    ("decode_runs", (64, 2048, 2048, 32, 8), "uniform"),
+]
+
 
 @pytest.fixture(scope="module")
 def mm():
@@ -70,6 +80,18 @@ def test_layer_dense_path_every_token(mm, name, shape, routing):
     counts = b.counts.cpu().numpy()
     say("  rows per expert: min %d max %d" % (counts.min(), counts.max()))
     assert counts.max() >= 64                        # at least one expert takes the dense kernel
+
+
+@pytest.mark.parametrize("name,shape,routing", DECODE, ids=[d[0] for d in DECODE])
+def test_layer_decode_path_every_token(mm, name, shape, routing):
+    T, H, I, E, k = shape
+    cfg = workloads.custom_config(name, 800 + [d[0] for d in DECODE].index(name), T, H, I, E, k,
+                                  routing=routing)
+    say("layer", name, cfg)
+    d = workloads.layer_inputs(cfg, 0)
+    b, ref, _ = check_layer(cfg, d["x_bits"], d["logits"], d, upload_weights(d))
+    counts = b.counts.cpu().numpy()
+    say("  rows per expert: min %d max %d" % (counts.min(), counts.max()))
 
 
 def test_layer_is_deterministic(mm):
