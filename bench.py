@@ -38,9 +38,17 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# Kernels that each entry point launches (a substring of the demangled name).
+ENTRY_KERNELS = {
+    "moe_mxfp4_gate_up_swiglu": ("k_decode<true>", "k_gate_up<", "k_dense<true>"),
+    "moe_mxfp4_down": ("k_decode<false>", "k_down<", "k_dense<false>"),
+}
+KERNEL_SOURCES = ("expert_decode.hip", "expert_stream.hip", "expert_dense.hip", "common.hpp")
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in ("expert_stream.hip", "common.hpp"):
+    for f in KERNEL_SOURCES:
         with open(os.path.join(ROOT, "mxfp4_moe_expert_route_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -82,6 +90,104 @@ def cpu_baseline(cfg, x_bits, logits, whost, budget_s):
                       % (done, cfg.T, cfg.name, elapsed)}
 
 
+def _csv_rows(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _find_csv(d, suffix):
+    for root, _, files in os.walk(d):
+        for fn in sorted(files):
+            if fn.endswith(suffix):
+                return os.path.join(root, fn)
+    raise FileNotFoundError("no *%s under %s" % (suffix, d))
+
+
+def _algorithmic_bytes(cfg, counts):
+    """Algorithmic HBM bytes of one call of each contraction entry point: the
+    touched experts' weights, plus the layer input x read once by gate/up (the
+    intermediates h and y could be fused away and are not counted)."""
+    T, H, I, k = cfg.T, cfg.H, cfg.I, cfg.k
+    touched = int((np.asarray(counts) > 0).sum())
+    w13 = 2 * I * H // 2 + 2 * I * H // 32
+    w2 = H * I // 2 + H * I // 32
+    return {"moe_mxfp4_gate_up_swiglu": touched * w13 + T * H * 2,
+            "moe_mxfp4_down": touched * w2, "touched": touched}
+
+
+def summarize_profiles(args):
+    """rocprofv3 output of bench.py runs -> the committed summaries.
+
+    Prints a markdown table of the kernel-trace statistics and, given the two
+    PMC runs (FETCH_SIZE, then WRITE_SIZE), stores in profiles/traffic.json the
+    calibrated HBM bytes per call of each contraction entry point.  The
+    counters are scaled by what they read for the largest weight clone
+    (a plain copy kernel of known size) in the same run."""
+    import workloads
+    cfg = workloads.CONFIGS[args.config]
+    out = ["# Kernel times and HBM traffic, %s workload (%d tokens, hidden %d, %d experts, "
+           "top-%d, intermediate %d)" % (cfg.name, cfg.T, cfg.H, cfg.E, cfg.k, cfg.I), ""]
+    if args.command:
+        out += ["Command (from /tmp, `TMPDIR=/tmp`, on one MI355X):", "", "```",
+                args.command, "```", ""]
+    if args.stats_dir:
+        rows = _csv_rows(_find_csv(args.stats_dir, "kernel_stats.csv"))
+        out += ["| kernel | calls | average (us) | min (us) | max (us) | share |",
+                "|---|---|---|---|---|---|"]
+        for r in rows:
+            name = r["Name"].replace("mxm::(anonymous namespace)::", "").replace(
+                "void ", "").split("(")[0]
+            out.append("| %s | %s | %.1f | %.1f | %.1f | %.1f%% |" % (
+                name, r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+                float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+        out.append("")
+    if args.fetch_dir and args.write_dir:
+        known = cfg.E * 2 * cfg.I * cfg.H // 2          # the w13 codes clone
+        per = {}
+        factors = {}
+        for ctr, d in (("FETCH_SIZE", args.fetch_dir), ("WRITE_SIZE", args.write_dir)):
+            rows = [r for r in _csv_rows(_find_csv(d, "counter_collection.csv"))
+                    if r["Counter_Name"] == ctr]
+            copies = [float(r["Counter_Value"]) for r in rows
+                      if "copyBuffer" in r["Kernel_Name"]]
+            factors[ctr] = known / (max(copies) * 1024.0)
+            for entry, pats in ENTRY_KERNELS.items():
+                by_kernel = {}
+                for r in rows:
+                    if any(p in r["Kernel_Name"] for p in pats):
+                        by_kernel.setdefault(r["Kernel_Name"], []).append(
+                            float(r["Counter_Value"]))
+                per.setdefault(entry, {})[ctr] = sum(
+                    np.mean(v) * 1024.0 * factors[ctr] for v in by_kernel.values())
+        alg = _algorithmic_bytes(cfg, np.load(args.counts) if args.counts else
+                                 np.full(cfg.E, 1))
+        path = os.path.join(ROOT, "profiles", "traffic.json")
+        db = json.load(open(path)) if os.path.exists(path) else {}
+        out += ["Calibration: the largest weight clone copies %d B; FETCH_SIZE reads %.4g KiB "
+                "for it (factor %.3f), WRITE_SIZE %.4g KiB (factor %.3f)."
+                % (known, known / 1024.0 / factors["FETCH_SIZE"], factors["FETCH_SIZE"],
+                   known / 1024.0 / factors["WRITE_SIZE"], factors["WRITE_SIZE"]), "",
+                "| entry point | fetched (MB/call) | written (MB/call) | total (MB/call) | "
+                "algorithmic (MB/call) | ratio |", "|---|---|---|---|---|---|"]
+        for entry, v in per.items():
+            tot = v["FETCH_SIZE"] + v["WRITE_SIZE"]
+            out.append("| %s | %.1f | %.1f | %.1f | %.1f | %.3f |" % (
+                entry, v["FETCH_SIZE"] / 1e6, v["WRITE_SIZE"] / 1e6, tot / 1e6,
+                alg[entry] / 1e6, tot / alg[entry]))
+            db["%s@%s" % (entry, cfg.name)] = {
+                "source_hash": kernel_source_hash(), "bytes_per_launch": int(round(tot)),
+                "fetch_bytes": int(round(v["FETCH_SIZE"])),
+                "write_bytes": int(round(v["WRITE_SIZE"])),
+                "algorithmic_bytes": int(alg[entry]),
+                "fetch_factor": round(factors["FETCH_SIZE"], 4),
+                "write_factor": round(factors["WRITE_SIZE"], 4)}
+        out.append("")
+        with open(path, "w") as f:
+            json.dump(db, f, indent=1, sort_keys=True)
+    print("\n".join(out))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -91,7 +197,21 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for cpu_baseline (0 disables)")
     ap.add_argument("--breakdown", action="store_true", help="per-kernel times on stderr")
+    ap.add_argument("--save-counts", default=None,
+                    help="write the per-expert row counts of the workload to this .npy")
+    ap.add_argument("--summarize", action="store_true",
+                    help="summarise rocprofv3 output (no GPU): --stats-dir, --fetch-dir, "
+                         "--write-dir, --counts, --command")
+    ap.add_argument("--stats-dir", default=None)
+    ap.add_argument("--fetch-dir", default=None)
+    ap.add_argument("--write-dir", default=None)
+    ap.add_argument("--counts", default=None)
+    ap.add_argument("--command", default=None)
     args = ap.parse_args()
+
+    if args.summarize:
+        summarize_profiles(args)
+        return
 
     if args.gpus != 1:
         print("bench.py: this build runs on exactly one GPU; --gpus %d is not supported "
@@ -160,6 +280,8 @@ def main():
         % (wall * 1e3 / steps, ms_step, gu_ms))
 
     counts = b.counts.cpu().numpy()
+    if args.save_counts:
+        np.save(args.save_counts, counts)
     touched = int((counts > 0).sum())
     w13_bytes = 2 * I * H // 2 + 2 * I * H // 32
     w2_bytes = H * I // 2 + H * I // 32
