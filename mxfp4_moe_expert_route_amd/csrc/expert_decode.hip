@@ -6,32 +6,38 @@
 // is the stream of FP4 weight bytes (§2 "FP4 Quantization": E2M1 codes with
 // an E8M0 scale per 32 weights).  To keep HBM saturated from the first byte
 // to the last, this kernel
-//   * keeps the weight stream in flight with asynchronous global->LDS loads
-//     issued by three loader waves into a ring of stages, so the depth of the
-//     stream does not depend on registers;
 //   * splits the work into units of 256 weight rows x the whole K of one
 //     tile (<= 16 token rows of one expert) and hands every workgroup an
 //     equal contiguous run of units; the stream crosses unit boundaries
 //     without a pause;
-//   * runs the contraction on MFMA waves that read codes, scales and
-//     activations from LDS (v_mfma_f32_16x16x32_bf16 after the scaled FP4 ->
-//     bf16 conversion), with one workgroup barrier per stage.
+//   * streams the codes with asynchronous global->LDS loads, issued by two
+//     loader waves into a ring of stages; a third loader wave brings each K
+//     chunk's activation rows and a fourth each unit's block scales (every
+//     loader wave waits only on its own loads);
+//   * runs the contraction on four MFMA waves (v_mfma_f32_16x16x32_bf16
+//     after the scaled FP4 -> bf16 conversion), one workgroup barrier per
+//     stage.
 //
-// Stage = 4 MX blocks (128 K elements) of the unit, 21 asynchronous loads:
-//   16 x codes  1 KB each: subtile i (16 rows) at i KB; lane L holds row L%16,
-//               block 4s + L/16 (the MFMA operand layout: each lane reads back
-//               its own 16 bytes)
-//    1 x scales one sixteenth of the scale chunk that follows the current one
-//    4 x acts   16 token rows x 256 bytes; the 16-byte chunk c of row j sits
-//               at position c ^ j, so lanes reading different rows hit
-//               different banks
-// Scales travel in chunks of 64 MX blocks (16 stages) x 256 rows: one load
-// covers 16 rows x 64 contiguous bytes, so it touches as few cache lines per
-// byte as the code loads.  Three chunk buffers: a chunk is loaded during the
-// previous chunk's stages, into the buffer freed two chunks before.
-// Accumulation order per output is that of the streaming kernel (MX block
-// 4s+g in lane group g, MFMA j over elements 8j..8j+7, steps in order), so the
-// results are the same bit for bit.
+// Stage = 64 weight rows (a row group) x 512 K elements (a K chunk: 256 code
+// bytes = 16 MX blocks per row).  A unit runs K chunk by K chunk and, within
+// a chunk, over its four row groups, so every load instruction reads 256
+// contiguous bytes of 4 rows: whole cache lines, long runs per DRAM page.
+//   codes   16 loads of 1 KB per stage; row r of the group keeps MX block b
+//           at 16-byte slot b ^ (r % 16), so the MFMA lanes (16 rows reading
+//           one block each) hit distinct banks
+//   acts    per K chunk, one 1 KB load per token row of the tile: row j keeps
+//           its 16-byte piece c at slot c ^ (j % 8); the MFMA waves read them
+//           into registers at the chunk's first row group and reuse them for
+//           the other three
+//   scales  per unit, the 256 rows' scale bytes as they lie in memory (two
+//           contiguous runs for gate/up, one for down), loaded whole-line in
+//           1 KB pieces; the MFMA waves read two chunks' 32 bytes per row at
+//           the first stage of every other chunk, so the buffer is free for
+//           the next unit's scales seven stages before the unit ends
+// MFMA wave w owns, in row group g, the weight rows 64g + 16w .. + 15 of the
+// unit: for gate/up the unit holds 128 gate columns then the same 128 up
+// columns, so the gate rows of group 0 (1) meet their up rows in group 2 (3)
+// inside the same wave.
 #include "common.hpp"
 
 namespace mxm {
@@ -44,37 +50,34 @@ typedef __attribute__((ext_vector_type(4))) int int4v;
 // vmcnt low bits 3:0, high bits 15:14; expcnt 6:4 and lgkmcnt 11:8 at max).
 #define MXM_VMCNT(n) ((((n) & 15) | (((n) >> 4) << 14)) | (7 << 4) | (15 << 8))
 
-#ifndef MXM_DEC_MW
-#define MXM_DEC_MW 4
-#endif
 #ifndef MXM_DEC_RING
 #define MXM_DEC_RING 4
 #endif
-constexpr int kMW = MXM_DEC_MW;                 // MFMA waves (4 or 8)
-constexpr int kNA = 16 / kMW;                   // 16-row weight subtiles per MFMA wave
-constexpr int kLW = 3;                          // loader waves
-constexpr int kThreadsDec = (kMW + kLW) * kWave;
-constexpr int kUnitRows = 256;                  // weight rows per unit (16 subtiles)
+constexpr int kMW = 4;                          // MFMA waves
+constexpr int kCW = 2;                          // code loader waves
+constexpr int kThreadsDec = (kMW + kCW + 2) * kWave;   // + activation and scale loaders
+constexpr int kUnitRows = 256;                  // weight rows per unit
+constexpr int kGroupRows = 64;                  // weight rows per stage
+constexpr int kChunkK = 512;                    // K elements per stage
 constexpr int kTokRows = 16;                    // token rows per tile
-constexpr int kCodesB = 16 * 1024;
-constexpr int kStageB = kCodesB + kTokRows * 256;
-constexpr int kRing = MXM_DEC_RING;             // stages in the LDS ring
-constexpr int kChunkSteps = 16;                 // stages per scale chunk (64 MX blocks)
-constexpr int kChunkB = kUnitRows * 64;
-constexpr int kGroup = 21;                      // asynchronous loads per stage
-constexpr int kPerLoader = kGroup / kLW;
+constexpr int kStageB = kGroupRows * kChunkK / 2;   // 16 KB of codes
+constexpr int kPerLoader = kStageB / 1024 / kCW;    // loads per code loader per stage
+constexpr int kRing = MXM_DEC_RING;
 constexpr int kMaxE = 1024;
+constexpr int kMaxK = 8192;
 constexpr int kMaxUnits = 64;                   // units per workgroup
-constexpr int kMaxTokIds = (kMaxUnits + 2) * kTokRows;
-constexpr int kLdsChunks = kRing * kStageB;
-constexpr int kLdsUnits = kLdsChunks + 3 * kChunkB;           // {e, nt, row0, rows} per unit
-constexpr int kLdsOffsets = kLdsUnits + kMaxUnits * 16;       // offsets[0..E]
-constexpr int kLdsTok = kLdsOffsets + (kMaxE + 1) * 4 + 12;   // token ids, 16 slots per tile
-constexpr int kLdsDec = kLdsTok + kMaxTokIds * 4;
-static_assert(kMW == 4 || kMW == 8, "MFMA waves");
-static_assert(kGroup % kLW == 0, "equal loads per loader wave");
-static_assert((kRing - 1) * kPerLoader + 16 <= 63, "vmcnt counts at most 63 loads");
-static_assert(kRing <= kChunkSteps, "chunk buffer reuse");
+constexpr int kMaxTiles = kMaxUnits + 2;        // tiles a run can touch
+constexpr int kLdsActs = kRing * kStageB;                       // 16 rows x 1 KB
+constexpr int kLdsScales = kLdsActs + kTokRows * 1024;          // 256 rows x K/32
+constexpr int kLdsUnits = kLdsScales + kUnitRows * (kMaxK / 32);
+constexpr int kLdsTok = kLdsUnits + kMaxUnits * 16;             // token ids, 16 per tile
+constexpr int kLdsDec = kLdsTok + kMaxTiles * kTokRows * 4;
+// set-up tables live in the activation buffer until the first chunk lands
+constexpr int kLdsOffs = kLdsActs;                              // offsets[0..E]
+constexpr int kLdsTpre = kLdsActs + (kMaxE + 4) * 4;            // tiles before expert e
+static_assert(kPerLoader * kCW * 1024 == kStageB, "whole loads per stage");
+static_assert((kRing - 2) * kPerLoader <= 63, "vmcnt counts at most 63 loads");
+static_assert(kLdsTpre + (kMaxE + 4) * 4 <= kLdsScales, "set-up tables fit the act buffer");
 static_assert(kLdsDec <= 160 * 1024, "LDS per CU");
 
 __device__ __forceinline__ lds_void* lds_at(uint8_t* base, int off) {
@@ -112,74 +115,45 @@ __device__ __forceinline__ int4v lds_read_i32x4(const uint8_t* p) {
   return v;
 }
 
-// Tiles of 16 rows over experts with 1 <= rows < hi (offsets in LDS; only
-// the MFMA waves call these).  Whole wave, uniform results.
-__device__ int count_tiles(const int* offs, int E, int hi) {
-  const int lane = lane_id();
-  int total = 0;
-  for (int c0 = 0; c0 < E; c0 += kWave) {
-    const int e = c0 + lane;
-    int cnt = e < E ? offs[e + 1] - offs[e] : 0;
-    if (cnt < 1 || cnt >= hi) cnt = 0;
-    const int incl = wave_incl_scan((cnt + kTokRows - 1) / kTokRows);
-    total += __shfl(incl, kWave - 1);
+// Expert of tile tau: the last e with tpre[e] <= tau (experts without tiles
+// have tpre[e] == tpre[e + 1] and are skipped by this rule).
+__device__ __forceinline__ int expert_of_tile(const int* tpre, int E, int tau) {
+  int lo = 0, hi = E;               // tpre[lo] <= tau < tpre[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (tpre[mid] <= tau) lo = mid;
+    else hi = mid;
   }
-  return __builtin_amdgcn_readfirstlane(total);
+  return lo;
 }
 
-__device__ Tile tile_at(const int* offs, int E, int hi, int tau) {
-  const int lane = lane_id();
-  Tile t{0, 0, 1};
-  int base = 0;
-  for (int c0 = 0; c0 < E; c0 += kWave) {
-    const int e = c0 + lane;
-    int off = 0, cnt = 0;
-    if (e < E) {
-      off = offs[e];
-      cnt = offs[e + 1] - off;
-    }
-    if (cnt < 1 || cnt >= hi) cnt = 0;
-    const int nt = (cnt + kTokRows - 1) / kTokRows;
-    const int incl = wave_incl_scan(nt);
-    const int total = __shfl(incl, kWave - 1);
-    if (tau < base + total) {
-      const int excl = base + incl - nt;
-      const unsigned long long m = __ballot(tau >= excl && tau < excl + nt);
-      const int src = __ffsll((long long)m) - 1;
-      const int ti = tau - __shfl(excl, src);
-      t.e = __builtin_amdgcn_readfirstlane(c0 + src);
-      t.row0 = __builtin_amdgcn_readfirstlane(__shfl(off, src) + ti * kTokRows);
-      t.rows = __builtin_amdgcn_readfirstlane(min(kTokRows, __shfl(cnt, src) - ti * kTokRows));
-      return t;
-    }
-    base += total;
-  }
-  return t;
-}
-
-// Weight row (within the whole tensor) of row r of unit subtile i (0..15) in
-// column block nt of expert e.  Gate/up: MFMA wave w = i / kNA owns kNA/2
-// column subtiles; its first kNA/2 subtiles are their gate rows, the others
-// the matching up rows.  Rows past the end are clamped to a valid row whose
-// results are never stored.
+// Row (within the whole weight tensor) of unit row u (0..255) of column block
+// nt of expert e.  Gate/up: unit rows 0..127 are gate columns 128 nt + u, rows
+// 128..255 the same up columns.  Down: rows 256 nt + u.
 template <bool GU>
-__device__ __forceinline__ int64_t weight_row(int e, int nt, int i, int r, int I, int H) {
+__device__ __forceinline__ int64_t weight_row(int e, int nt, int u, int I, int H) {
   if constexpr (GU) {
-    constexpr int kHalf = kNA / 2;
-    const int w = i / kNA, a = i % kNA;
-    const int col = min(nt * 128 + w * 16 * kHalf + 16 * (a % kHalf) + r, I - 1);
-    return int64_t(e) * 2 * I + (a >= kHalf ? I : 0) + col;
+    const int col = min(nt * 128 + (u & 127), I - 1);
+    return int64_t(e) * 2 * I + (u >= 128 ? I : 0) + col;
   } else {
-    return int64_t(e) * H + min(nt * kUnitRows + 16 * i + r, H - 1);
+    return int64_t(e) * H + min(nt * kUnitRows + u, H - 1);
   }
 }
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
 
+// byte b of each of the four dwords, packed
+__device__ __forceinline__ uint32_t pick_bytes(uint4 v, int b) {
+  const int sh = 8 * b;
+  return ((v.x >> sh) & 0xffu) | (((v.y >> sh) & 0xffu) << 8) | (((v.z >> sh) & 0xffu) << 16) |
+         (((v.w >> sh) & 0xffu) << 24);
+}
+
 // GU: act = x (bf16 [T, H]), K = H, out = h (bf16 [R, I]).
 // !GU: act = h (bf16 [R, I]), K = I, out = y (fp32 [R, H]).
-// Requires K % 2048 == 0 and a run of at most kMaxUnits units per workgroup.
-// Experts with fewer than `hi` rows take part.
+// Requires K % 512 == 0, K <= kMaxK, I % 128 == 0, H % 256 == 0 and a run of
+// at most kMaxUnits units per workgroup.  Experts with fewer than `hi` rows
+// take part.
 template <bool GU>
 __global__ __launch_bounds__(kThreadsDec) void k_decode(
     const uint16_t* __restrict__ act, const int32_t* __restrict__ sorted_pairs,
@@ -187,122 +161,146 @@ __global__ __launch_bounds__(kThreadsDec) void k_decode(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, void* __restrict__ out,
     int ntile_n, int hi) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = lane_id();
   const int r16 = lane & 15, g = lane >> 4;
-  const int nsteps = K / 128;
   const int nblk = K / 32;
-  int* offs = reinterpret_cast<int*>(lds + kLdsOffsets);
+  const int S = 4 * (K / kChunkK);                 // stages per unit
+  int* offs = reinterpret_cast<int*>(lds + kLdsOffs);
+  int* tpre = reinterpret_cast<int*>(lds + kLdsTpre);
   int* tok_ids = reinterpret_cast<int*>(lds + kLdsTok);
   int4v* units = reinterpret_cast<int4v*>(lds + kLdsUnits);
 
-  // ---- set-up (MFMA waves; loaders issue no global loads besides their
-  // asynchronous ones): expert offsets, then the run's unit table and the
-  // token ids of its tiles
-  if (wave < kMW)
-    for (int i = threadIdx.x; i <= E; i += kMW * kWave) offs[i] = offsets[i];
+  // ---- set-up: expert offsets, tiles per expert, the run's unit table
+  for (int i = tid; i <= E; i += kThreadsDec) offs[i] = offsets[i];
+  __syncthreads();
+  if (wave == 0) {
+    int base = 0;
+    for (int c0 = 0; c0 < E; c0 += kWave) {
+      const int e = c0 + lane;
+      int cnt = e < E ? offs[e + 1] - offs[e] : 0;
+      if (cnt < 1 || cnt >= hi) cnt = 0;
+      const int nt = (cnt + kTokRows - 1) / kTokRows;
+      const int incl = wave_incl_scan(nt);
+      if (e < E) tpre[e] = base + incl - nt;
+      base += __shfl(incl, kWave - 1);
+    }
+    if (lane == 0) tpre[E] = base;
+  }
   __syncthreads();
   const int G = gridDim.x;
-  int u0 = 0, u1 = 0;
-  if (wave < kMW) {
-    const int U = count_tiles(offs, E, hi) * ntile_n;
-    u0 = int((int64_t(U) * blockIdx.x) / G);
-    u1 = int((int64_t(U) * (blockIdx.x + 1)) / G);
-    if (u1 > u0) {
-      const int tau0 = u0 / ntile_n;
-      for (int tau = tau0 + wave; tau <= (u1 - 1) / ntile_n; tau += kMW) {
-        const Tile t = tile_at(offs, E, hi, tau);
-        if (GU && lane < t.rows)
-          tok_ids[(tau - tau0) * kTokRows + lane] = sorted_pairs[t.row0 + lane] / k;
-        const int ua = max(u0, tau * ntile_n), ub = min(u1, (tau + 1) * ntile_n);
-        if (lane < ub - ua) units[ua - u0 + lane] = int4v{t.e, ua + lane - tau * ntile_n, t.row0, t.rows};
-      }
-    }
-    if (wave == 0 && lane == 0) {
-      offs[kMaxE + 1] = u0;         // the run, for the loader waves
-      offs[kMaxE + 2] = u1;
-    }
+  const int U = tpre[E] * ntile_n;
+  const int u0 = __builtin_amdgcn_readfirstlane(int((int64_t(U) * blockIdx.x) / G));
+  const int u1 = __builtin_amdgcn_readfirstlane(int((int64_t(U) * (blockIdx.x + 1)) / G));
+  const int nu = u1 - u0;
+  const int tau0 = u0 / ntile_n;
+  for (int idx = tid; idx < nu; idx += kThreadsDec) {
+    const int u = u0 + idx;
+    const int tau = u / ntile_n;
+    const int e = expert_of_tile(tpre, E, tau);
+    const int ti = tau - tpre[e];
+    const int row0 = offs[e] + ti * kTokRows;
+    units[idx] = int4v{e, u - tau * ntile_n, row0, min(kTokRows, offs[e + 1] - row0)};
   }
   __syncthreads();
-  if (wave >= kMW) {
-    u0 = lds_read_i32(lds + kLdsOffsets + 4 * (kMaxE + 1));
-    u1 = lds_read_i32(lds + kLdsOffsets + 4 * (kMaxE + 2));
-  }
-  u0 = __builtin_amdgcn_readfirstlane(u0);
-  u1 = __builtin_amdgcn_readfirstlane(u1);
-  const int nu = u1 - u0;
-  const int Q = nu * nsteps;                              // stages of the run
+  const int Q = nu * S;                            // stages of the run
   if (Q == 0) return;
-  const int tau0 = u0 / ntile_n;
-  const int nchunk = nu * (nsteps / kChunkSteps);         // scale chunks of the run
+  const int pre = min(kRing - 1, Q);
+
+  if (wave == kMW + kCW + 1) {
+    // ---------------- scale loader ----------------
+    const int half = 128 * nblk;                   // bytes of 128 rows (a multiple of 1 KB)
+    const int nsl = kUnitRows * nblk / 1024;       // 1 KB loads per unit
+    auto issue_scales = [&](int j, int m0, int m1) {
+      const int4v ui = lds_read_i32x4(lds + kLdsUnits + 16 * j);
+      for (int m = m0; m < m1; ++m) {
+        const int o = 1024 * m + 16 * lane;
+        const uint8_t* src;
+        if constexpr (GU) {
+          const int h2 = o >= half;
+          src = scales + weight_row<true>(ui.x, ui.y, h2 ? 128 : 0, I, H) * nblk + (o - h2 * half);
+        } else {
+          src = scales + weight_row<false>(ui.x, ui.y, 0, I, H) * nblk + o;
+        }
+        __builtin_amdgcn_global_load_lds(src, lds_at(lds, kLdsScales + 1024 * m), 16, 0, 0);
+      }
+    };
+    issue_scales(0, 0, nsl);
+    __builtin_amdgcn_s_barrier();                  // token ids are in LDS
+    __builtin_amdgcn_s_waitcnt(MXM_VMCNT(0));
+    for (int q = 0; q < Q; ++q) {
+      __builtin_amdgcn_s_barrier();
+      const int jq = q / S, sq = q - jq * S;
+      // the unit's last scale read is at its stage S - 8; the next unit's
+      // scales go out in three parts at stages S - 7 .. S - 5
+      const int part = sq - (S - 7);
+      if (jq + 1 < nu && part >= 0 && part < 3)
+        issue_scales(jq + 1, nsl * part / 3, nsl * (part + 1) / 3);
+      if (sq == S - 1) __builtin_amdgcn_s_waitcnt(MXM_VMCNT(0));
+    }
+    return;
+  }
+
+  if (wave == kMW + kCW) {
+    // ---------------- activation loader ----------------
+    auto issue_acts = [&](int j, int kc) {
+      const int4v ui = lds_read_i32x4(lds + kLdsUnits + 16 * j);
+      const int slot = (u0 + j) / ntile_n - tau0;
+      for (int jj = 0; jj < ui.w; ++jj) {
+        int64_t row;
+        if constexpr (GU) row = lds_read_i32(lds + kLdsTok + 4 * (slot * kTokRows + jj));
+        else row = int64_t(ui.z) + jj;
+        const int c = lane ^ (jj & 7);             // piece stored at slot `lane`
+        const uint8_t* src = reinterpret_cast<const uint8_t*>(act) +
+                             (row * K + int64_t(kc) * kChunkK) * 2 + c * 16;
+        __builtin_amdgcn_global_load_lds(src, lds_at(lds, kLdsActs + 1024 * jj), 16, 0, 0);
+      }
+    };
+    __builtin_amdgcn_s_barrier();                  // token ids are in LDS
+    issue_acts(0, 0);
+    __builtin_amdgcn_s_waitcnt(MXM_VMCNT(0));
+    for (int q = 0; q < Q; ++q) {
+      __builtin_amdgcn_s_barrier();
+      // a chunk's rows are read at its first stage; the next chunk goes out
+      // three stages before its first stage, after that read
+      const int p = q + 3;
+      if (p < Q && (p & 3) == 0) {
+        const int jn = p / S, sn = p - jn * S;
+        issue_acts(jn, sn >> 2);
+      }
+      if (((q + 1) & 3) == 0) __builtin_amdgcn_s_waitcnt(MXM_VMCNT(0));
+    }
+    return;
+  }
 
   if (wave >= kMW) {
-    // ---------------- loader waves ----------------
+    // ---------------- code loaders ----------------
     const int ld = wave - kMW;
-    // unit info (e, nt, row0, rows) of the run's unit j
-    auto unit = [&](int j) { return lds_read_i32x4(lds + kLdsUnits + 16 * j); };
-    // activation row of token slot jj of unit info ui
-    auto act_row = [&](const int4v& ui, int j, int jj) -> int64_t {
-      const int jc = min(jj, ui.w - 1);
-      if constexpr (GU) {
-        const int tau = (u0 + j) / ntile_n;
-        return lds_read_i32(lds + kLdsTok + 4 * ((tau - tau0) * kTokRows + jc));
-      } else {
-        return int64_t(ui.z) + jc;
-      }
-    };
-    // scale chunk x (index in the run): load j (= subtile j: 16 rows x 64 B)
-    auto issue_scale = [&](int x, int jld, int xbuf) {
-      const int xu = min(x, nchunk - 1);                    // past the end: harmless reload
-      const int cpu = nsteps / kChunkSteps;
-      const int ju = xu / cpu, c = xu - ju * cpu;
-      const int4v ui = unit(ju);
-      const uint8_t* src = scales + weight_row<GU>(ui.x, ui.y, jld, lane >> 2, I, H) * nblk +
-                           64 * c + 16 * (lane & 3);
-      __builtin_amdgcn_global_load_lds(src, lds_at(lds, kLdsChunks + (xbuf % 3) * kChunkB + 1024 * jld),
-                                       16, 0, 0);
-    };
-    // chunk 0: loads j = ld, ld + 3, ... before the first stage group
-    for (int j = ld; j < 16; j += kLW) issue_scale(0, j, 0);
-    // cached per unit: this lane's source of each owned load at step 0
-    const uint8_t* src[kPerLoader];
     int cur = -1;
-    auto issue = [&](int p) {                               // stage group p
-      const int j = p / nsteps, s = p - j * nsteps;
+    int4v ui{0, 0, 0, 1};
+    auto issue = [&](int p) {
+      const int j = p / S, s = p - j * S;
       if (j != cur) {
         cur = j;
-        const int4v ui = unit(j);
-#pragma unroll
-        for (int m = 0; m < kPerLoader; ++m) {
-          const int idx = ld + kLW * m;
-          if (idx < 16) {
-            src[m] = codes + weight_row<GU>(ui.x, ui.y, idx, r16, I, H) * (K / 2) + g * 16;
-          } else if (idx > 16) {
-            const int mm = idx - 17, jj = 4 * mm + (lane >> 4), pos = lane & 15;
-            const int c = pos ^ jj;                          // logical chunk stored at pos
-            src[m] = reinterpret_cast<const uint8_t*>(act) +
-                     (act_row(ui, j, jj) * K + (c >> 2) * 32 + (c & 3) * 8) * 2;
-          }
-        }
+        ui = lds_read_i32x4(lds + kLdsUnits + 16 * j);
       }
+      const int kc = s >> 2, rg = s & 3;
       uint8_t* st = lds + (p % kRing) * kStageB;
 #pragma unroll
       for (int m = 0; m < kPerLoader; ++m) {
-        const int idx = ld + kLW * m;
-        if (idx < 16) {
-          __builtin_amdgcn_global_load_lds(src[m] + s * 64, lds_at(st, idx * 1024), 16, 0, 0);
-        } else if (idx == 16) {
-          const int x = j * (nsteps / kChunkSteps) + s / kChunkSteps;   // chunk of stage p
-          issue_scale(x + 1, s % kChunkSteps, x + 1);
-        } else {
-          __builtin_amdgcn_global_load_lds(src[m] + s * 256, lds_at(st, kCodesB + 1024 * (idx - 17)),
-                                           16, 0, 0);
-        }
+        const int i = ld + kCW * m;                // load i: rows 4i..4i+3 of the group
+        const int rr = 4 * i + (lane >> 4);
+        const int blk = (lane & 15) ^ (rr & 15);
+        const uint8_t* src = codes +
+                             weight_row<GU>(ui.x, ui.y, kGroupRows * rg + rr, I, H) * (K / 2) +
+                             kc * (kChunkK / 2) + blk * 16;
+        __builtin_amdgcn_global_load_lds(src, lds_at(st, i * 1024), 16, 0, 0);
       }
     };
-    const int pre = min(kRing - 1, Q);
     for (int p = 0; p < pre; ++p) issue(p);
-    vmcnt_wait_stages<kPerLoader, kRing - 2>(pre - 1);     // chunk 0 and stage 0 landed
+    __builtin_amdgcn_s_barrier();                  // token ids are in LDS
+    vmcnt_wait_stages<kPerLoader, kRing - 2>(pre - 1);   // stage 0 landed
     for (int q = 0; q < Q; ++q) {
       __builtin_amdgcn_s_barrier();
       if (q + kRing - 1 < Q) issue(q + kRing - 1);
@@ -312,78 +310,107 @@ __global__ __launch_bounds__(kThreadsDec) void k_decode(
   }
 
   // ---------------- MFMA waves ----------------
+  if constexpr (GU) {
+    const int ntl = (u1 - 1) / ntile_n - tau0 + 1;
+    for (int idx = tid; idx < ntl * kTokRows; idx += kMW * kWave) {
+      const int tau = tau0 + idx / kTokRows, jj = idx % kTokRows;
+      const int e = expert_of_tile(tpre, E, tau);
+      const int row0 = offs[e] + (tau - tpre[e]) * kTokRows;
+      if (row0 + jj < offs[e + 1]) tok_ids[idx] = sorted_pairs[row0 + jj] / k;
+    }
+  }
+  __syncthreads();                                 // token ids are in LDS
+
   const int w = wave;
-  f32x4 acc[kNA];
+  const uint8_t* scb = lds + kLdsScales;
+  const uint8_t* actb = lds + kLdsActs;
+  f32x4 acc[4];
+  uint32_t sc4[2][4];
+  uint4 xb[4][4];
   int4v ui{0, 0, 0, 1};
-  int s = 0, j = 0, x = 0;
-  for (int q = 0; q < Q; ++q) {
-    if (s == 0) {
-      ui = units[j];
+  int j = 0, s = 0;
+  // S is a multiple of 8: two K chunks of four row groups per iteration
+  for (int q0 = 0; q0 < Q; q0 += 8) {
 #pragma unroll
-      for (int a = 0; a < kNA; ++a) acc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    __builtin_amdgcn_s_barrier();
-    const uint8_t* st = lds + (q % kRing) * kStageB;
-    const uint8_t* sc = lds + kLdsChunks + (x % 3) * kChunkB;
-    uint4 cw[kNA];
-    uint32_t sb[kNA];
-    uint4 xb[4];
+    for (int st8 = 0; st8 < 8; ++st8) {
+      const int q = q0 + st8;
+      const int par = st8 >> 2, rg = st8 & 3;
+      if (st8 == 0 && s == 0) {
+        ui = units[j];
 #pragma unroll
-    for (int a = 0; a < kNA; ++a) {
-      const int i = w * kNA + a;
-      cw[a] = *reinterpret_cast<const uint4*>(st + i * 1024 + 16 * lane);
-      sb[a] = sc[(16 * i + r16) * 64 + ((4 * s + g) & 63)];
-    }
-    const int jr = min(r16, ui.w - 1);
+        for (int a = 0; a < 4; ++a) acc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      __builtin_amdgcn_s_barrier();
+      if (st8 == 0) {
+        // scale bytes of this chunk and the next: blocks 16 kc + 4t + g
+        const int kc = s >> 2;
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
-      xb[m] = *reinterpret_cast<const uint4*>(st + kCodesB + jr * 256 + 16 * ((4 * g + m) ^ jr));
+        for (int a = 0; a < 4; ++a) {
+          const uint8_t* sp = scb + (kGroupRows * a + 16 * w + r16) * nblk + 16 * kc;
+          sc4[0][a] = pick_bytes(*reinterpret_cast<const uint4*>(sp), g);
+          sc4[1][a] = pick_bytes(*reinterpret_cast<const uint4*>(sp + 16), g);
+        }
+      }
+      if (rg == 0) {
+        const int jr = min(r16, ui.w - 1);
 #pragma unroll
-    for (int a = 0; a < kNA; ++a) {
-      const float scl = e8m0_to_f32(sb[a]);
-      const uint32_t c4[4] = {cw[a].x, cw[a].y, cw[a].z, cw[a].w};
+        for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int m = 0; m < 4; ++m)
-        acc[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dequant8(c4[m], scl), as_bf16x8(xb[m]),
-                                                         acc[a], 0, 0, 0);
-    }
-    ++s;
-    if (s % kChunkSteps == 0) ++x;
-    if (s == nsteps) {
-      // lane holds D[4g+v][r16]: weight row 4g+v of the subtile, token row r16
-      const int nt = ui.y, row0 = ui.z, rows = ui.w;
-      if (r16 < rows) {
-        if constexpr (GU) {
-          constexpr int kHalf = kNA / 2;
-          uint16_t* h = reinterpret_cast<uint16_t*>(out);
-#pragma unroll
-          for (int a = 0; a < kHalf; ++a) {
-            const int col = nt * 128 + w * 16 * kHalf + 16 * a + 4 * g;
-            if (col < I) {
-              const f32x4 gv = acc[a], uv = acc[a + kHalf];
-              const uint32_t h0 = f32_to_bf16_rne(silu_mul(gv[0], uv[0]));
-              const uint32_t h1 = f32_to_bf16_rne(silu_mul(gv[1], uv[1]));
-              const uint32_t h2 = f32_to_bf16_rne(silu_mul(gv[2], uv[2]));
-              const uint32_t h3 = f32_to_bf16_rne(silu_mul(gv[3], uv[3]));
-              *reinterpret_cast<uint2*>(h + size_t(row0 + r16) * I + col) =
-                  make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
-            }
+          for (int m = 0; m < 4; ++m) {
+            const int c = 16 * t + 4 * g + m;
+            xb[t][m] = *reinterpret_cast<const uint4*>(actb + jr * 1024 + ((c ^ (jr & 7)) * 16));
           }
-        } else {
-          float* y = reinterpret_cast<float*>(out);
+      }
+      const uint8_t* st = lds + (q % kRing) * kStageB + (16 * w + r16) * (kChunkK / 2);
+      uint4 cw[4];
 #pragma unroll
-          for (int a = 0; a < kNA; ++a) {
-            const int n = nt * kUnitRows + 16 * (w * kNA + a) + 4 * g;
-            if (n < H) {
-              const f32x4 v = acc[a];
-              *reinterpret_cast<float4*>(y + size_t(row0 + r16) * H + n) =
-                  make_float4(v[0], v[1], v[2], v[3]);
+      for (int t = 0; t < 4; ++t)
+        cw[t] = *reinterpret_cast<const uint4*>(st + (((4 * t + g) ^ r16) * 16));
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float scl = e8m0_to_f32((sc4[par][rg] >> (8 * t)) & 0xffu);
+        const uint32_t c4[4] = {cw[t].x, cw[t].y, cw[t].z, cw[t].w};
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          acc[rg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dequant8(c4[m], scl),
+                                                            as_bf16x8(xb[t][m]), acc[rg], 0, 0, 0);
+      }
+      ++s;
+      if (st8 == 7 && s == S) {
+        // lane holds D[4g+v][r16]: weight row 4g+v of the subtile, token row r16
+        const int nt = ui.y, row0 = ui.z, rows = ui.w;
+        if (r16 < rows) {
+          if constexpr (GU) {
+            uint16_t* h = reinterpret_cast<uint16_t*>(out);
+#pragma unroll
+            for (int a = 0; a < 2; ++a) {
+              const int col = nt * 128 + kGroupRows * a + 16 * w + 4 * g;
+              if (col < I) {
+                const f32x4 gv = acc[a], uv = acc[a + 2];
+                const uint32_t h0 = f32_to_bf16_rne(silu_mul(gv[0], uv[0]));
+                const uint32_t h1 = f32_to_bf16_rne(silu_mul(gv[1], uv[1]));
+                const uint32_t h2 = f32_to_bf16_rne(silu_mul(gv[2], uv[2]));
+                const uint32_t h3 = f32_to_bf16_rne(silu_mul(gv[3], uv[3]));
+                *reinterpret_cast<uint2*>(h + size_t(row0 + r16) * I + col) =
+                    make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+              }
+            }
+          } else {
+            float* y = reinterpret_cast<float*>(out);
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+              const int n = nt * kUnitRows + kGroupRows * a + 16 * w + 4 * g;
+              if (n < H) {
+                const f32x4 v = acc[a];
+                *reinterpret_cast<float4*>(y + size_t(row0 + r16) * H + n) =
+                    make_float4(v[0], v[1], v[2], v[3]);
+              }
             }
           }
         }
+        s = 0;
+        ++j;
       }
-      s = 0;
-      ++j;
     }
   }
 }
@@ -421,7 +448,7 @@ hipError_t launch_decode(const uint16_t* act, const int32_t* sp, const int32_t* 
     attr_set = true;
   }
   const int K = GU ? H : I;
-  const int ntile_n = GU ? (I + 127) / 128 : (H + kUnitRows - 1) / kUnitRows;
+  const int ntile_n = GU ? I / 128 : H / kUnitRows;
   k_decode<GU><<<dim3(unsigned(cu_count())), kThreadsDec, kLdsDec, s>>>(
       act, sp, off, K, I, H, E, k, c, sc, out, ntile_n, hi);
   return hipGetLastError();
@@ -430,10 +457,10 @@ hipError_t launch_decode(const uint16_t* act, const int32_t* sp, const int32_t* 
 }  // namespace
 
 bool decode_supported(int T, int H, int I, int E, int k) {
-  if (H % 2048 || I % 2048 || E > kMaxE) return false;
+  if (H % 2048 || I % 2048 || H > kMaxK || I > kMaxK || E > kMaxE) return false;
   const int R = T * k;
   return max_units_per_wg(R, E, I / 128) <= kMaxUnits &&
-         max_units_per_wg(R, E, (H + kUnitRows - 1) / kUnitRows) <= kMaxUnits;
+         max_units_per_wg(R, E, H / kUnitRows) <= kMaxUnits;
 }
 
 hipError_t launch_gate_up_decode(const uint16_t* x, const int32_t* sorted_pairs,
