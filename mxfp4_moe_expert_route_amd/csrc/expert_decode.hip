@@ -66,12 +66,10 @@ constexpr int kRing = MXM_DEC_RING;
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 8192;
 constexpr int kMaxUnits = 64;                   // units per workgroup
-constexpr int kMaxTiles = kMaxUnits + 2;        // tiles a run can touch
 constexpr int kLdsActs = kRing * kStageB;                       // 16 rows x 1 KB
 constexpr int kLdsScales = kLdsActs + kTokRows * 1024;          // 256 rows x K/32
 constexpr int kLdsUnits = kLdsScales + kUnitRows * (kMaxK / 32);
-constexpr int kLdsTok = kLdsUnits + kMaxUnits * 16;             // token ids, 16 per tile
-constexpr int kLdsDec = kLdsTok + kMaxTiles * kTokRows * 4;
+constexpr int kLdsDec = kLdsUnits + kMaxUnits * 16;
 // set-up tables live in the activation buffer until the first chunk lands
 constexpr int kLdsOffs = kLdsActs;                              // offsets[0..E]
 constexpr int kLdsTpre = kLdsActs + (kMaxE + 4) * 4;            // tiles before expert e
@@ -169,7 +167,6 @@ __global__ __launch_bounds__(kThreadsDec) void k_decode(
   const int S = 4 * (K / kChunkK);                 // stages per unit
   int* offs = reinterpret_cast<int*>(lds + kLdsOffs);
   int* tpre = reinterpret_cast<int*>(lds + kLdsTpre);
-  int* tok_ids = reinterpret_cast<int*>(lds + kLdsTok);
   int4v* units = reinterpret_cast<int4v*>(lds + kLdsUnits);
 
   // ---- set-up: expert offsets, tiles per expert, the run's unit table
@@ -194,7 +191,6 @@ __global__ __launch_bounds__(kThreadsDec) void k_decode(
   const int u0 = __builtin_amdgcn_readfirstlane(int((int64_t(U) * blockIdx.x) / G));
   const int u1 = __builtin_amdgcn_readfirstlane(int((int64_t(U) * (blockIdx.x + 1)) / G));
   const int nu = u1 - u0;
-  const int tau0 = u0 / ntile_n;
   for (int idx = tid; idx < nu; idx += kThreadsDec) {
     const int u = u0 + idx;
     const int tau = u / ntile_n;
@@ -227,7 +223,6 @@ __global__ __launch_bounds__(kThreadsDec) void k_decode(
       }
     };
     issue_scales(0, 0, nsl);
-    __builtin_amdgcn_s_barrier();                  // token ids are in LDS
     __builtin_amdgcn_s_waitcnt(MXM_VMCNT(0));
     for (int q = 0; q < Q; ++q) {
       __builtin_amdgcn_s_barrier();
@@ -244,12 +239,20 @@ __global__ __launch_bounds__(kThreadsDec) void k_decode(
 
   if (wave == kMW + kCW) {
     // ---------------- activation loader ----------------
+    // gate/up: lane jj keeps the token of row jj of the current tile, fetched
+    // when the unit's tile changes (three stages before its first chunk)
+    int tok = 0, tok_row0 = -1;
     auto issue_acts = [&](int j, int kc) {
       const int4v ui = lds_read_i32x4(lds + kLdsUnits + 16 * j);
-      const int slot = (u0 + j) / ntile_n - tau0;
+      if constexpr (GU) {
+        if (ui.z != tok_row0) {
+          tok_row0 = ui.z;
+          tok = sorted_pairs[ui.z + min(lane, ui.w - 1)] / k;
+        }
+      }
       for (int jj = 0; jj < ui.w; ++jj) {
         int64_t row;
-        if constexpr (GU) row = lds_read_i32(lds + kLdsTok + 4 * (slot * kTokRows + jj));
+        if constexpr (GU) row = __builtin_amdgcn_readlane(tok, jj);
         else row = int64_t(ui.z) + jj;
         const int c = lane ^ (jj & 7);             // piece stored at slot `lane`
         const uint8_t* src = reinterpret_cast<const uint8_t*>(act) +
@@ -257,7 +260,6 @@ __global__ __launch_bounds__(kThreadsDec) void k_decode(
         __builtin_amdgcn_global_load_lds(src, lds_at(lds, kLdsActs + 1024 * jj), 16, 0, 0);
       }
     };
-    __builtin_amdgcn_s_barrier();                  // token ids are in LDS
     issue_acts(0, 0);
     __builtin_amdgcn_s_waitcnt(MXM_VMCNT(0));
     for (int q = 0; q < Q; ++q) {
@@ -299,7 +301,6 @@ __global__ __launch_bounds__(kThreadsDec) void k_decode(
       }
     };
     for (int p = 0; p < pre; ++p) issue(p);
-    __builtin_amdgcn_s_barrier();                  // token ids are in LDS
     vmcnt_wait_stages<kPerLoader, kRing - 2>(pre - 1);   // stage 0 landed
     for (int q = 0; q < Q; ++q) {
       __builtin_amdgcn_s_barrier();
@@ -310,17 +311,6 @@ __global__ __launch_bounds__(kThreadsDec) void k_decode(
   }
 
   // ---------------- MFMA waves ----------------
-  if constexpr (GU) {
-    const int ntl = (u1 - 1) / ntile_n - tau0 + 1;
-    for (int idx = tid; idx < ntl * kTokRows; idx += kMW * kWave) {
-      const int tau = tau0 + idx / kTokRows, jj = idx % kTokRows;
-      const int e = expert_of_tile(tpre, E, tau);
-      const int row0 = offs[e] + (tau - tpre[e]) * kTokRows;
-      if (row0 + jj < offs[e + 1]) tok_ids[idx] = sorted_pairs[row0 + jj] / k;
-    }
-  }
-  __syncthreads();                                 // token ids are in LDS
-
   const int w = wave;
   const uint8_t* scb = lds + kLdsScales;
   const uint8_t* actb = lds + kLdsActs;
