@@ -1,5 +1,5 @@
 // Grouped MXFP4 expert contractions for experts with many rows (prefill-like
-// batches): an LDS-tiled bf16 MFMA GEMM with the FP4 weights dequantised from
+// batches): a persistent bf16 MFMA GEMM with the FP4 weights dequantised from
 // LDS, fused with SwiGLU (gate/up) or writing fp32 (down).
 //
 // The pages put the experts in MXFP4 (block 32) with bf16 activations
@@ -7,73 +7,65 @@
 // tokens reach each expert the contraction is compute-bound and runs on the
 // bf16 matrix cores with fp32 accumulation.
 //
-// Workgroup: one tile of up to 256 rows of one expert x 128 weight rows.
-// Eleven waves with separate jobs, so that each has its own in-order load
-// counter:
-//   waves 0-7  MFMA: a 4 x 2 grid, each wave 64 rows (4 interleaved 16-row
-//              subtiles) x 64 weight rows (4 subtiles), 64 fp32 accumulators;
-//              two MFMA waves per SIMD hide each other's LDS and barrier waits
-//   waves 8-9  activations: global -> LDS ring of kRA stages (buffer loads
-//              straight into LDS; rows past the tile's end are out of range
-//              and cost no memory traffic)
-//   wave  10   weights: codes and scale chunks -> LDS ring of kRW stages
-//              (global loads straight into LDS, far ahead of use: they come
-//              from HBM)
-// A stage is 64 of K (two MX blocks); one barrier per stage hands the ring
-// slots from the loaders to the MFMA waves and back.
+// Work items: (expert, n-tile of 256 weight rows, m-tile of 256 token rows).
+// Items are ordered expert by expert, n-tile by n-tile, m-tile fastest, and
+// the list is cut into eight equal contiguous ranges, one per XCD (workgroup
+// b runs on XCD b % 8).  The workgroups of an XCD (one per CU) take its items
+// round-robin, so at any time they work on neighbouring items: the n-tiles of
+// one m-tile read the same activation rows from that XCD's L2.  An m-tile
+// covers every row of a typical expert, so each weight byte leaves HBM once.
 //
-// Register roles follow v_mfma_f32_16x16x32_bf16: weights are operand A (row
-// = weight row), activations operand B (row = tile row).  In stage s, lane
-// group g covers elements 16g..16g+15 of the stage, MFMA j the 8 from 16g+8j;
-// weights and activations use the same assignment.
+// The loads are sized by cache lines, the currency of the CU's load path: a
+// stage reads 32 code bytes of each weight row and 128 activation bytes (one
+// line) of each token row; the scale bytes of a row arrive 16 at a time (8
+// stages' worth) in a separate chunk buffer.
 //
-// LDS layouts are swizzled so that the MFMA waves' reads hit distinct banks
-// (128-byte bank rows): activation row r keeps its 16-byte chunk c in slot
-// c ^ (r & 7); weight row r keeps its two 16-byte blocks swapped when bit 2
-// of r is set.
+// Workgroup: 8 waves in a 2 x 4 grid, two per SIMD; wave (wn, wm) computes
+// 128 weight rows (8 subtiles of 16) x 64 token rows (the 16-row subtiles wm,
+// wm+4, wm+8, wm+12 of the tile), 128 fp32 accumulators per lane.  For
+// gate/up the workgroup's 256 weight rows are 128 gate columns and the same
+// 128 up columns; wave wn holds 64 of each, so SwiGLU pairs inside the wave.
 //
-// Workgroup order is XCD-aware: consecutive workgroups go to different XCDs,
-// so tile tau and its column tiles are given to one XCD, where they run back
-// to back and share that XCD's L2 copy of the tile's activation rows.
+// A stage is 64 of K (two MX blocks).  Every wave issues its share of the
+// stage's asynchronous global->LDS loads (1 KB of codes, 4 x 1 KB of
+// activations, and every 8 stages, for waves 0-3, 1 KB of scales) two stages
+// ahead into a ring of three, then computes the current stage: one barrier
+// per stage.
+//
+// Register roles follow v_mfma_f32_16x16x32_bf16: weights are operand A
+// (row = weight row), activations operand B (row = token row).  In a stage,
+// lane group g covers K elements 16g..16g+15 (half of MX block g/2), MFMA kk
+// the 8 from 16g+8kk; weights and activations use the same assignment.
+//
+// LDS layouts are swizzled so that the MFMA waves' reads spread over the
+// banks: token row r keeps its 16-byte chunk c in slot c ^ (r & 7); weight
+// row r keeps its two 16-byte blocks swapped when bit 2 of r is set.
 #include "common.hpp"
 
 namespace mxm {
 namespace {
 
-// Tunables (compile-time; defaults are the measured best on MI355X).
-#ifndef MXM_DENSE_MT
-#define MXM_DENSE_MT 256
-#endif
-#ifndef MXM_DENSE_RA
-#define MXM_DENSE_RA 4
-#endif
-#ifndef MXM_DENSE_RW
-#define MXM_DENSE_RW 6
-#endif
-constexpr int kMT = MXM_DENSE_MT;    // rows per tile (a multiple of 64: 4 row waves x 16)
-constexpr int kNT = 128;             // weight rows per workgroup
+constexpr int kMT = 256;             // token rows per tile
+constexpr int kNT = 256;             // weight rows per tile
 constexpr int kKS = 64;              // K per stage (2 MX blocks)
-constexpr int kRA = MXM_DENSE_RA;    // activation ring depth, stages
-constexpr int kRW = MXM_DENSE_RW;    // weight ring depth, stages
-constexpr int kMSub = kMT / 64;      // row subtiles per MFMA wave
-constexpr int kAInstr = kMT / 16;    // 16-byte loads per lane per stage, per activation loader
-constexpr int kScStages = 8;         // stages per scale chunk (16 blocks = 16 B per row)
-constexpr int kMmaWaves = 8;
-constexpr int kDThreads = 11 * kWave;
+constexpr int kRing = 3;             // stages in the LDS ring
+constexpr int kWaves = 8;
+constexpr int kDThreads = kWaves * kWave;
 constexpr int kMinRows = 64;         // experts with fewer rows use the streaming kernels
-
-constexpr int kAStage = kMT * kKS * 2;            // 32 KB at 256 rows
-constexpr int kWStage = kNT * kKS / 2;            // 4 KB
-constexpr int kSChunk = kNT * 16;                 // 2 KB
-constexpr int kLdsW = kRA * kAStage;
-constexpr int kLdsS = kLdsW + kRW * kWStage;
-constexpr int kLdsBytes = kLdsS + 2 * kSChunk;    // 132 KB at the defaults
-static_assert(kMT % 64 == 0 && kMSub <= 4, "tile rows");
-static_assert(kLdsBytes <= 160 * 1024, "LDS");
-static_assert((kRA - 2) * kAInstr <= 63 && (kRW - 2) * 4 <= 63, "vmcnt range");
-// the two scale-chunk slots are reused 16 stages apart: chunk q+2 is issued
-// kRW-1 stages before stage 8q+16, after chunk q's last use at stage 8q+7
-static_assert(kRW <= 9, "scale chunk ring");
+constexpr int kMaxE = 1024;
+constexpr int kWB = kNT * kKS / 2;   // 8 KB of codes per stage
+constexpr int kAB = kMT * kKS * 2;   // 32 KB of activations per stage
+constexpr int kStage = kWB + kAB;
+constexpr int kScStages = 8;         // stages per scale chunk (16 blocks = 16 B per row)
+constexpr int kSChunk = kNT * 16;    // 4 KB
+constexpr int kLdsS = kRing * kStage;
+constexpr int kLdsMpre = kLdsS + 2 * kSChunk;
+constexpr int kLdsBytes = kLdsMpre + (kMaxE + 4) * 4;
+constexpr int kLoadsPerStage = 5;    // per wave: 1 code and 4 activation loads
+static_assert(kLdsBytes <= 160 * 1024, "LDS per CU");
+static_assert(kWB == kWaves * 1024 && kAB == 4 * kWaves * 1024 && kSChunk == 4 * 1024,
+              "every wave issues the same stage loads; waves 0-3 one scale load each");
+static_assert((kRing - 2) * kLoadsPerStage <= 63, "vmcnt range");
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -81,243 +73,212 @@ typedef __attribute__((address_space(3))) void lds_void;
 // vmcnt low bits 3:0, high bits 15:14; expcnt 6:4 and lgkmcnt 11:8 at max).
 #define MXM_VMCNT(n) ((((n) & 15) | (((n) >> 4) << 14)) | (7 << 4) | (15 << 8))
 
-// s_waitcnt for "at most STAGES * n loads outstanding", n a runtime count in
-// [0, NMAX] (the immediate must be a constant, hence the switch).
-template <int STAGES, int NMAX>
+__device__ __forceinline__ lds_void* lds_at(uint8_t* base, int off) {
+  return (lds_void*)(base + off);   // generic -> LDS address space
+}
+
+// at most PER * n loads of this wave outstanding, n in [0, NMAX]
+template <int PER, int NMAX>
 __device__ __forceinline__ void vmcnt_wait_stages(int n) {
   if constexpr (NMAX > 0) {
-    if (n == NMAX) {
-      __builtin_amdgcn_s_waitcnt(MXM_VMCNT(STAGES * NMAX));
+    if (n >= NMAX) {
+      __builtin_amdgcn_s_waitcnt(MXM_VMCNT(PER * NMAX));
       return;
     }
-    vmcnt_wait_stages<STAGES, NMAX - 1>(n);
+    vmcnt_wait_stages<PER, NMAX - 1>(n);
   } else {
     __builtin_amdgcn_s_waitcnt(MXM_VMCNT(0));
   }
 }
 
-__device__ __forceinline__ lds_void* lds_at(uint8_t* base, int off) {
-  return (lds_void*)(base + off);   // generic -> LDS address space
-}
-
-// The MFMA waves' K loop for NV valid row subtiles (wm, wm+4, ...): one
-// barrier per stage, then dequantise this wave's 4 weight subtiles from LDS
-// and run NV x 4 x 2 MFMAs against the activation subtiles.
-template <int NV>
-__device__ __forceinline__ void mma_kloop(const uint8_t* lds, int nst, int wm, int g, int r16,
-                                          const int (&wl)[4], f32x4 (&acc)[4][4]) {
-  __builtin_amdgcn_s_barrier();
-  for (int s = 0; s < nst; ++s) {
-    const uint8_t* wst = lds + kLdsW + (s % kRW) * kWStage;
-    const uint8_t* sch = lds + kLdsS + ((s / kScStages) & 1) * kSChunk;
-    const uint8_t* ast = lds + (s % kRA) * kAStage;
-    const int sblk = (s % kScStages) * 2 + (g >> 1);
-    // issue every LDS read of the stage first: weight codes and scales of the
-    // 4 weight subtiles, activation operands of both K halves
-    uint2 cw[4];
-    uint32_t sb[4];
-#pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const int row = wl[a] + r16;
-      const int slot = 2 * row + ((g >> 1) ^ ((row >> 2) & 1));
-      cw[a] = *reinterpret_cast<const uint2*>(wst + slot * 16 + 8 * (g & 1));
-      sb[a] = sch[row * 16 + sblk];
-    }
-    uint4 b[2][NV > 0 ? NV : 1];
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        const int m = (wm + 4 * i) * 16 + r16;
-        const int slot = (2 * g + jj) ^ (m & 7);
-        b[jj][i] = *reinterpret_cast<const uint4*>(ast + m * 128 + slot * 16);
-      }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-      bf16x8 wa[4];
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-        wa[a] = dequant8(jj ? cw[a].y : cw[a].x, e8m0_to_f32(sb[a]));
-#pragma unroll
-      for (int i = 0; i < NV; ++i)
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-          acc[i][a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[a], as_bf16x8(b[jj][i]),
-                                                              acc[i][a], 0, 0, 0);
-    }
-    __builtin_amdgcn_s_barrier();
+// Expert of m-tile tau: the last e with mpre[e] <= tau.
+__device__ __forceinline__ int expert_of(const int* mpre, int E, int tau) {
+  int lo = 0, hi = E;               // mpre[lo] <= tau < mpre[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (mpre[mid] <= tau) lo = mid;
+    else hi = mid;
   }
+  return lo;
 }
 
+// Local weight row (0..255 within the n-tile) of subtile a of wave wn.
 template <bool GU>
-__global__ __launch_bounds__(kDThreads) void k_dense(
-    const uint16_t* __restrict__ act, uint32_t act_bytes, const int32_t* __restrict__ sorted_pairs,
-    const int32_t* __restrict__ offsets, int K, int I, int H, int E, int k,
-    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, void* __restrict__ out,
-    int ntile_n, int min_rows) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+__device__ __forceinline__ int local_row(int wn, int a) {
+  if constexpr (GU) return a < 4 ? 64 * wn + 16 * a : 128 + 64 * wn + 16 * (a - 4);
+  else return 128 * wn + 16 * a;
+}
+
+// Row in the whole weight tensor of local row r of n-tile n of expert e:
+// gate/up n-tiles are 128 gate columns then the same 128 up columns.
+template <bool GU>
+__device__ __forceinline__ int64_t weight_row(int e, int n, int r, int I, int H) {
+  if constexpr (GU) return int64_t(e) * 2 * I + (r < 128 ? 0 : I) + 128 * n + (r & 127);
+  else return int64_t(e) * H + kNT * n + r;
+}
+
+struct Item {
+  int e, n, row0, rows;
+};
+
+// One work item: K loop over the ring, then the epilogue.  NV = this wave's
+// valid token subtiles (wm, wm+4, ... below the tile's row count).
+template <bool GU, int NV>
+__device__ __forceinline__ void run_item(uint8_t* lds, const Item& it, int K, int I, int H, int k,
+                                         const __amdgpu_buffer_rsrc_t& rs,
+                                         const int32_t* __restrict__ sorted_pairs,
+                                         const uint8_t* __restrict__ codes,
+                                         const uint8_t* __restrict__ scales, void* __restrict__ out) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = lane_id();
-
-  // XCD-aware tile order: blockIdx % 8 picks the XCD.
-  const int xcd = blockIdx.x & 7;
-  const int j = blockIdx.x >> 3;
-  const int lt = j / ntile_n;
-  const int nt = j - lt * ntile_n;
-  Tile t;
-  if (!find_tile(offsets, E, kMT, lt * 8 + xcd, t, min_rows)) return;   // whole workgroup
-  t.e = __builtin_amdgcn_readfirstlane(t.e);
-  t.row0 = __builtin_amdgcn_readfirstlane(t.row0);
-  t.rows = __builtin_amdgcn_readfirstlane(t.rows);
-
+  const int r16 = lane & 15, g = lane >> 4;
+  const int wn = wave & 1, wm = wave >> 1;
   const int nst = K / kKS;
-  const int NW = GU ? 2 * I : H;                  // weight rows per expert
-  // weight row (within the expert) of local row r of this workgroup's 128
-  auto wrow = [&](int r) {
-    if (GU) return r < 64 ? 64 * nt + r : I + 64 * nt + (r - 64);
-    return kNT * nt + r;
+  const int nblk = K / 32;
+
+  // ---- this lane's load sources
+  // activations: loads j = wave + 8q cover tile rows 8j..8j+7; lane -> row
+  // 8j + lane/8, slot lane%8 holding chunk (lane%8) ^ (row&7).  Rows past the
+  // tile's end get 2^31 added: out of the buffer's range, no memory traffic.
+  uint32_t voff[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int tr = 8 * (wave + kWaves * q) + (lane >> 3);
+    const int row = it.row0 + min(tr, it.rows - 1);
+    const uint32_t src = GU ? uint32_t(sorted_pairs[row] / k) : uint32_t(row);
+    voff[q] = src * uint32_t(K * 2) + uint32_t((((lane & 7) ^ (tr & 7))) * 16) +
+              (uint32_t(tr >= it.rows) << 31);
+  }
+  // codes: load i = wave covers local rows 32i..32i+31; lane -> row
+  // 32i + lane/2, slot parity lane&1 holding block (lane&1) ^ ((row>>2)&1)
+  const uint8_t* wsrc;
+  {
+    const int r = 32 * wave + (lane >> 1);
+    const int b = (lane & 1) ^ ((r >> 2) & 1);
+    wsrc = codes + weight_row<GU>(it.e, it.n, r, I, H) * (K / 2) + b * 16;
+  }
+  // scales (waves 0-3): local rows 64 wave + lane, 16 bytes (8 stages) each
+  const bool scl_wave = wave < 4;
+  const uint8_t* ssrc =
+      scales + weight_row<GU>(it.e, it.n, 64 * (wave & 3) + lane, I, H) * nblk;
+
+  auto issue_scales = [&](int c) {            // chunk c: stages 8c..8c+7
+    if (scl_wave)
+      __builtin_amdgcn_global_load_lds(ssrc + 16 * c,
+                                       lds_at(lds, kLdsS + (c & 1) * kSChunk + 1024 * wave), 16,
+                                       0, 0);
+  };
+  auto issue = [&](int s) {
+    uint8_t* st = lds + (s % kRing) * kStage;
+    __builtin_amdgcn_global_load_lds(wsrc + s * 32, lds_at(st, 1024 * wave), 16, 0, 0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds_at(st, kWB + 1024 * (wave + kWaves * q)),
+                                               16, voff[q] + uint32_t(s * kKS * 2), 0, 0, 0);
   };
 
-  if (wave == kMmaWaves + 2) {
-    // ---------------- weight loader ----------------
-    const uint8_t* cb = codes + size_t(t.e) * NW * (K / 2);
-    const uint8_t* sb = scales + size_t(t.e) * NW * (K / 32);
-    const uint8_t* crow[4];
-    for (int i = 0; i < 4; ++i) {
-      const int c = i * kWave + lane;                 // LDS slot (16 bytes) of the stage
-      const int r = c >> 1;                           // local weight row
-      const int blk = (c & 1) ^ ((r >> 2) & 1);       // which of the row's 2 blocks sits here
-      crow[i] = cb + size_t(wrow(r)) * (K / 2) + blk * 16;
+  f32x4 acc[8][NV > 0 ? NV : 1];
+#pragma unroll
+  for (int a = 0; a < 8; ++a)
+#pragma unroll
+    for (int i = 0; i < NV; ++i) acc[a][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // every subtile row's place in the stage
+  int wslot[8], srow[8];
+#pragma unroll
+  for (int a = 0; a < 8; ++a) {
+    const int row = local_row<GU>(wn, a) + r16;
+    wslot[a] = 16 * (2 * row + ((g >> 1) ^ ((row >> 2) & 1))) + 8 * (g & 1);
+    srow[a] = 16 * row + (g >> 1);
+  }
+  int aoff[NV > 0 ? NV : 1][2];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int tr = 16 * (wm + 4 * i) + r16;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) aoff[i][kk] = tr * 128 + (((2 * g + kk) ^ (tr & 7)) * 16);
+  }
+
+  // Issue order: chunk 0, stage 0, stage 1, then per iteration s the next
+  // stage s + 2, preceded every 8 stages (s % 8 == 0) by scale chunk s/8 + 1
+  // (the buffer of chunk s/8 - 1, whose last stage s - 1 is done).  nst is a
+  // multiple of 8.
+  static_assert(kRing == 3, "one stage in flight behind the current one");
+  issue_scales(0);
+  issue(0);
+  issue(1);
+  for (int s = 0; s < nst; ++s) {
+    // this wave's loads of stage s (and everything issued before) have landed;
+    // those issued after them (stage s + 1 and maybe a scale chunk) may still
+    // be on the way
+    if (s + 1 < nst) {
+      if (scl_wave && s % kScStages == 1 && s - 1 + kScStages < nst)
+        __builtin_amdgcn_s_waitcnt(MXM_VMCNT(kLoadsPerStage + 1));
+      else
+        __builtin_amdgcn_s_waitcnt(MXM_VMCNT(kLoadsPerStage));
+    } else {
+      __builtin_amdgcn_s_waitcnt(MXM_VMCNT(0));
     }
-    const uint8_t* srow[2];
-    for (int i = 0; i < 2; ++i) srow[i] = sb + size_t(wrow(i * kWave + lane)) * (K / 32);
-    auto issue = [&](int st) {
-      if (st % kScStages == 0) {                      // scale chunk before the codes
-        const int q = st / kScStages;
-        for (int i = 0; i < 2; ++i)
-          __builtin_amdgcn_global_load_lds(srow[i] + q * 16,
-                                           lds_at(lds, kLdsS + (q & 1) * kSChunk + i * 1024), 16,
-                                           0, 0);
-      }
-      for (int i = 0; i < 4; ++i)
-        __builtin_amdgcn_global_load_lds(crow[i] + st * 32,
-                                         lds_at(lds, kLdsW + (st % kRW) * kWStage + i * 1024), 16,
-                                         0, 0);
-    };
-    for (int st = 0; st < kRW - 1; ++st) issue(st);   // nst >= kRW (host check)
-    __builtin_amdgcn_s_waitcnt(MXM_VMCNT((kRW - 2) * 4));
     __builtin_amdgcn_s_barrier();
-    for (int s = 0; s < nst; ++s) {
-      if (s + kRW - 1 < nst) {
-        issue(s + kRW - 1);
-        __builtin_amdgcn_s_waitcnt(MXM_VMCNT((kRW - 2) * 4));   // stage s+1 has landed
-      } else {
-        __builtin_amdgcn_s_waitcnt(MXM_VMCNT(0));
+    if (s + kRing - 1 < nst) {
+      if (s % kScStages == 0 && s + kScStages < nst) issue_scales(s / kScStages + 1);
+      issue(s + kRing - 1);
+    }
+    if constexpr (NV > 0) {
+      const uint8_t* st = lds + (s % kRing) * kStage;
+      uint2 cw[8];
+      uint32_t sb[8];
+#pragma unroll
+      for (int a = 0; a < 8; ++a) {
+        cw[a] = *reinterpret_cast<const uint2*>(st + wslot[a]);
+        sb[a] = lds[kLdsS + ((s / kScStages) & 1) * kSChunk + srow[a] + 2 * (s % kScStages)];
       }
-      __builtin_amdgcn_s_barrier();
+      uint4 b[2][NV];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+          b[kk][i] = *reinterpret_cast<const uint4*>(st + kWB + aoff[i][kk]);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int a = 0; a < 8; ++a) {
+          const bf16x8 wa = dequant8(kk ? cw[a].y : cw[a].x, e8m0_to_f32(sb[a]));
+#pragma unroll
+          for (int i = 0; i < NV; ++i)
+            acc[a][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, as_bf16x8(b[kk][i]), acc[a][i],
+                                                                0, 0, 0);
+        }
     }
-    return;
   }
 
-  if (wave >= kMmaWaves) {
-    // ---------------- activation loaders (waves 8, 9) ----------------
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(act), 0, int(act_bytes), 0x00020000);
-    const int half = wave - kMmaWaves;                 // which half of the stage's rows
-    uint32_t voff[kAInstr];                            // per chunk: row byte + swizzled chunk
-    for (int i = 0; i < kAInstr; ++i) {
-      const int c = half * kAInstr * kWave + i * kWave + lane;   // chunk of the stage = LDS slot
-      const int r = c >> 3;                            // tile row
-      const int gc = (c & 7) ^ (r & 7);                // global 16-byte chunk kept in slot c
-      const int row = t.row0 + min(r, t.rows - 1);    // unconditional, in-bounds read
-      const uint32_t src = GU ? uint32_t(sorted_pairs[row] / k) : uint32_t(row);
-      // rows past the tile's end get 2^31 added: out of the buffer's range
-      // (act_bytes + K*2 < 2^31), so they cost no memory traffic
-      voff[i] = src * uint32_t(K * 2) + uint32_t(gc * 16) + (uint32_t(r >= t.rows) << 31);
-    }
-    // one load instruction covers 8 tile rows: skip the ones wholly past the
-    // tile's end (their LDS rows are never read)
-    const int na = __builtin_amdgcn_readfirstlane(
-        max(0, min(kAInstr, (t.rows - half * kAInstr * 8 + 7) >> 3)));
-    auto issue = [&](int st) {
-      for (int i = 0; i < kAInstr; ++i)
-        if (i < na)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(
-              rs, lds_at(lds, (st % kRA) * kAStage + (half * kAInstr + i) * kWave * 16), 16,
-              voff[i] + uint32_t(st * kKS * 2), 0, 0, 0);
-    };
-    // wait until at most (kRA-2) stages of this wave's loads are outstanding
-    auto wait_lead = [&]() { vmcnt_wait_stages<kRA - 2, kAInstr>(na); };
-    for (int st = 0; st < kRA - 1; ++st) issue(st);
-    wait_lead();
-    __builtin_amdgcn_s_barrier();
-    for (int s = 0; s < nst; ++s) {
-      if (s + kRA - 1 < nst) {
-        issue(s + kRA - 1);
-        wait_lead();
-      } else {
-        __builtin_amdgcn_s_waitcnt(MXM_VMCNT(0));
-      }
-      __builtin_amdgcn_s_barrier();
-    }
-    return;
-  }
-
-  // ---------------- MFMA waves 0-7 ----------------
-  const int wm = wave & 3;
-  const int wn = wave >> 2;
-  const int r16 = lane & 15;
-  const int g = lane >> 4;
-  const int nsub = (t.rows + 15) >> 4;
-  const int nvalid = max(0, min(kMSub, (nsub - wm + 3) >> 2));  // subtiles wm, wm+4, ... in range
-  int wl[4];                                                 // local weight row of subtile a
+  // epilogue: lane holds D[4g+v][r16]: weight row 4g+v of subtile a, token
+  // row r16 of subtile wm + 2i
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
-    wl[a] = GU ? (a < 2 ? 32 * wn + 16 * a : 64 + 32 * wn + 16 * (a - 2)) : 64 * wn + 16 * a;
-
-  f32x4 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int a = 0; a < 4; ++a) acc[i][a] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // The K loop is instantiated per count of valid row subtiles so that its
-  // body has no branch and the compiler can keep LDS reads ahead of MFMAs.
-  switch (nvalid) {
-    case 4: mma_kloop<4>(lds, nst, wm, g, r16, wl, acc); break;
-    case 3: mma_kloop<3>(lds, nst, wm, g, r16, wl, acc); break;
-    case 2: mma_kloop<2>(lds, nst, wm, g, r16, wl, acc); break;
-    case 1: mma_kloop<1>(lds, nst, wm, g, r16, wl, acc); break;
-    default: mma_kloop<0>(lds, nst, wm, g, r16, wl, acc); break;
-  }
-
-  // epilogue: lane holds D[4g+v][r16] = output column base + 4g + v of tile row m
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = (wm + 4 * i) * 16 + r16;
-    if (m >= t.rows) continue;
-    const size_t row = size_t(t.row0 + m);
-    if (GU) {
+  for (int i = 0; i < NV; ++i) {
+    const int m = 16 * (wm + 4 * i) + r16;
+    if (m >= it.rows) continue;
+    const size_t row = size_t(it.row0 + m);
+    if constexpr (GU) {
       uint16_t* h = static_cast<uint16_t*>(out);
 #pragma unroll
-      for (int a = 0; a < 2; ++a) {
-        const f32x4 gv = acc[i][a];
-        const f32x4 uv = acc[i][a + 2];
+      for (int a = 0; a < 4; ++a) {
+        const f32x4 gv = acc[a][i];
+        const f32x4 uv = acc[a + 4][i];
         uint32_t hv[4];
 #pragma unroll
         for (int v = 0; v < 4; ++v)
           hv[v] = f32_to_bf16_rne(gv[v] / (1.0f + __expf(-gv[v])) * uv[v]);
-        const int col = 64 * nt + 32 * wn + 16 * a + 4 * g;
+        const int col = 128 * it.n + 64 * wn + 16 * a + 4 * g;
         *reinterpret_cast<uint2*>(h + row * I + col) =
             make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
       }
     } else {
       float* y = static_cast<float*>(out);
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const f32x4 v = acc[i][a];
-        const int col = kNT * nt + 64 * wn + 16 * a + 4 * g;
+      for (int a = 0; a < 8; ++a) {
+        const f32x4 v = acc[a][i];
+        const int col = kNT * it.n + 128 * wn + 16 * a + 4 * g;
         *reinterpret_cast<float4*>(y + row * H + col) = make_float4(v[0], v[1], v[2], v[3]);
       }
     }
@@ -325,9 +286,81 @@ __global__ __launch_bounds__(kDThreads) void k_dense(
 }
 
 template <bool GU>
+__global__ __launch_bounds__(kDThreads, 1) void k_dense(
+    const uint16_t* __restrict__ act, uint32_t act_bytes, const int32_t* __restrict__ sorted_pairs,
+    const int32_t* __restrict__ offsets, int K, int I, int H, int E, int k,
+    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, void* __restrict__ out,
+    int min_rows) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = lane_id();
+  const int wm = wave >> 1;
+  int* mpre = reinterpret_cast<int*>(lds + kLdsMpre);
+  const int ntn = GU ? 2 * I / kNT : H / kNT;       // n-tiles per expert
+
+  // m-tiles before each expert (experts with at least min_rows rows)
+  if (wave == 0) {
+    int base = 0;
+    for (int c0 = 0; c0 < E; c0 += kWave) {
+      const int e = c0 + lane;
+      const int cnt = e < E ? offsets[e + 1] - offsets[e] : 0;
+      const int mt = cnt >= min_rows ? (cnt + kMT - 1) / kMT : 0;
+      const int incl = wave_incl_scan(mt);
+      if (e < E) mpre[e] = base + incl - mt;
+      base += __shfl(incl, kWave - 1);
+    }
+    if (lane == 0) mpre[E] = base;
+  }
+  __syncthreads();
+  const int nitems = mpre[E] * ntn;
+  const int xcd = blockIdx.x & 7;
+  const int gx = __builtin_amdgcn_readfirstlane(int(gridDim.x >> 3));   // workgroups per XCD
+  const int v0 = int(int64_t(nitems) * xcd / 8);
+  const int v1 = int(int64_t(nitems) * (xcd + 1) / 8);
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(act), 0, int(act_bytes), 0x00020000);
+
+  for (int v = v0 + int(blockIdx.x >> 3); v < v1; v += gx) {
+    const int tau = v / ntn;
+    const int e = expert_of(mpre, E, tau);
+    const int mt = mpre[e + 1] - mpre[e];
+    const int local = v - mpre[e] * ntn;
+    const int n = local / mt, m = local - n * mt;
+    Item it;
+    it.e = __builtin_amdgcn_readfirstlane(e);
+    it.n = __builtin_amdgcn_readfirstlane(n);
+    const int off0 = offsets[e];
+    it.row0 = __builtin_amdgcn_readfirstlane(off0 + m * kMT);
+    it.rows = __builtin_amdgcn_readfirstlane(min(kMT, offsets[e + 1] - off0 - m * kMT));
+    const int nsub = (it.rows + 15) >> 4;
+    const int nv = __builtin_amdgcn_readfirstlane(max(0, min(4, (nsub - wm + 3) >> 2)));
+    switch (nv) {
+      case 4: run_item<GU, 4>(lds, it, K, I, H, k, rs, sorted_pairs, codes, scales, out); break;
+      case 3: run_item<GU, 3>(lds, it, K, I, H, k, rs, sorted_pairs, codes, scales, out); break;
+      case 2: run_item<GU, 2>(lds, it, K, I, H, k, rs, sorted_pairs, codes, scales, out); break;
+      case 1: run_item<GU, 1>(lds, it, K, I, H, k, rs, sorted_pairs, codes, scales, out); break;
+      default: run_item<GU, 0>(lds, it, K, I, H, k, rs, sorted_pairs, codes, scales, out); break;
+    }
+    __syncthreads();                 // the ring is free for the next item
+  }
+}
+
+int cu_count() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v < 1)
+      v = 256;
+    n = v;
+  }
+  return n;
+}
+
+template <bool GU>
 hipError_t launch_dense(const uint16_t* act, uint32_t act_bytes, const int32_t* sorted_pairs,
-                        const int32_t* offsets, int T, int H, int I, int E, int k,
-                        const uint8_t* codes, const uint8_t* scales, void* out, hipStream_t s) {
+                        const int32_t* offsets, int H, int I, int E, int k, const uint8_t* codes,
+                        const uint8_t* scales, void* out, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_dense<GU>),
@@ -335,28 +368,21 @@ hipError_t launch_dense(const uint16_t* act, uint32_t act_bytes, const int32_t* 
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const int R = T * k;
   const int K = GU ? H : I;
-  const int ntile_n = GU ? I / 64 : H / kNT;
-  // tiles: experts with >= kMinRows rows, each cut into tiles of kMT rows
-  const int big = min(E, R / kMinRows);
-  int slots = big + R / kMT + 1;
-  slots = (slots + 7) / 8 * 8;
-  const int64_t grid = int64_t(slots) * ntile_n;
+  const int grid = (cu_count() + 7) / 8 * 8;      // one per CU, a multiple of 8
   k_dense<GU><<<dim3(unsigned(grid)), kDThreads, kLdsBytes, s>>>(
-      act, act_bytes, sorted_pairs, offsets, K, I, H, E, k, codes, scales, out, ntile_n, kMinRows);
+      act, act_bytes, sorted_pairs, offsets, K, I, H, E, k, codes, scales, out, kMinRows);
   return hipGetLastError();
 }
 
 }  // namespace
 
-// The dense path needs K and the column tiles to be whole stages, scale
-// chunks and rings, and byte offsets of activation rows that fit the 31-bit
-// range of buffer addressing.
+// The dense path needs K to be whole scale chunks, the n-tiles whole (128
+// gate columns, 256 output rows), E within the LDS table and byte offsets of
+// activation rows that fit the 31-bit range of buffer addressing.
 bool dense_supported(int T, int H, int I, int E, int k) {
-  (void)E;
   const int64_t R = int64_t(T) * k;
-  if (H % 512 || I % 512) return false;
+  if (H % 512 || I % 512 || E > kMaxE) return false;
   if (int64_t(T) * H * 2 + H * 2 >= (int64_t(1) << 31)) return false;
   if (R * I * 2 + I * 2 >= (int64_t(1) << 31)) return false;
   return R >= kMinRows;
@@ -368,14 +394,14 @@ hipError_t launch_gate_up_dense(const uint16_t* x, const int32_t* sorted_pairs,
                                 const int32_t* offsets, int T, int H, int I, int E, int k,
                                 const uint8_t* codes, const uint8_t* scales, uint16_t* h,
                                 hipStream_t s) {
-  return launch_dense<true>(x, uint32_t(int64_t(T) * H * 2), sorted_pairs, offsets, T, H, I, E, k,
+  return launch_dense<true>(x, uint32_t(int64_t(T) * H * 2), sorted_pairs, offsets, H, I, E, k,
                             codes, scales, h, s);
 }
 
 hipError_t launch_down_dense(const uint16_t* h, const int32_t* offsets, int T, int H, int I,
                              int E, int k, const uint8_t* codes, const uint8_t* scales, float* y,
                              hipStream_t s) {
-  return launch_dense<false>(h, uint32_t(int64_t(T) * k * I * 2), nullptr, offsets, T, H, I, E, k,
+  return launch_dense<false>(h, uint32_t(int64_t(T) * k * I * 2), nullptr, offsets, H, I, E, k,
                              codes, scales, y, s);
 }
 
