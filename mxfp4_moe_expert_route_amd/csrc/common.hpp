@@ -15,6 +15,12 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// Workgroup barrier for kernels that manage their own s_waitcnt: no counter
+// is waited on, and the "memory" clobber keeps the compiler from moving this
+// wave's loads and stores across it (the s_barrier intrinsic alone does not,
+// and LDS filled by asynchronous global->LDS loads must not be read early).
+__device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
 // fp32 -> bf16 bits, round to nearest even; NaN -> canonical quiet NaN.
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);

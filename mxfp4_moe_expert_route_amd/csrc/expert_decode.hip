@@ -225,7 +225,7 @@ __global__ __launch_bounds__(kThreadsDec) void k_decode(
     issue_scales(0, 0, nsl);
     __builtin_amdgcn_s_waitcnt(MXM_VMCNT(0));
     for (int q = 0; q < Q; ++q) {
-      __builtin_amdgcn_s_barrier();
+      wg_barrier();
       const int jq = q / S, sq = q - jq * S;
       // the unit's last scale read is at its stage S - 8; the next unit's
       // scales go out in three parts at stages S - 7 .. S - 5
@@ -263,7 +263,7 @@ __global__ __launch_bounds__(kThreadsDec) void k_decode(
     issue_acts(0, 0);
     __builtin_amdgcn_s_waitcnt(MXM_VMCNT(0));
     for (int q = 0; q < Q; ++q) {
-      __builtin_amdgcn_s_barrier();
+      wg_barrier();
       // a chunk's rows are read at its first stage; the next chunk goes out
       // three stages before its first stage, after that read
       const int p = q + 3;
@@ -303,7 +303,7 @@ __global__ __launch_bounds__(kThreadsDec) void k_decode(
     for (int p = 0; p < pre; ++p) issue(p);
     vmcnt_wait_stages<kPerLoader, kRing - 2>(pre - 1);   // stage 0 landed
     for (int q = 0; q < Q; ++q) {
-      __builtin_amdgcn_s_barrier();
+      wg_barrier();
       if (q + kRing - 1 < Q) issue(q + kRing - 1);
       if (q + 1 < Q) vmcnt_wait_stages<kPerLoader, kRing - 2>(min(q + kRing - 1, Q - 1) - (q + 1));
     }
@@ -330,7 +330,7 @@ __global__ __launch_bounds__(kThreadsDec) void k_decode(
 #pragma unroll
         for (int a = 0; a < 4; ++a) acc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
-      __builtin_amdgcn_s_barrier();
+      wg_barrier();
       if (st8 == 0) {
         // scale bytes of this chunk and the next: blocks 16 kc + 4t + g
         const int kc = s >> 2;

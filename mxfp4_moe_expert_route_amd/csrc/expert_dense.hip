@@ -7,7 +7,7 @@
 // tokens reach each expert the contraction is compute-bound and runs on the
 // bf16 matrix cores with fp32 accumulation.
 //
-// Work items: (expert, n-tile of 256 weight rows, m-tile of 256 token rows).
+// Work items: (expert, n-tile of 256 weight rows, m-tile of 192 token rows).
 // Items are ordered expert by expert, n-tile by n-tile, m-tile fastest, and
 // the list is cut into eight equal contiguous ranges, one per XCD (workgroup
 // b runs on XCD b % 8).  The workgroups of an XCD (one per CU) take its items
@@ -21,16 +21,17 @@
 // stages' worth) in a separate chunk buffer.
 //
 // Workgroup: 8 waves in a 2 x 4 grid, two per SIMD; wave (wn, wm) computes
-// 128 weight rows (8 subtiles of 16) x 64 token rows (the 16-row subtiles wm,
-// wm+4, wm+8, wm+12 of the tile), 128 fp32 accumulators per lane.  For
-// gate/up the workgroup's 256 weight rows are 128 gate columns and the same
-// 128 up columns; wave wn holds 64 of each, so SwiGLU pairs inside the wave.
+// 128 weight rows (8 subtiles of 16) x 48 token rows (the 16-row subtiles wm,
+// wm+4, wm+8 of the tile), 96 fp32 accumulators per lane.  For gate/up the
+// workgroup's 256 weight rows are 128 gate columns and the same 128 up
+// columns; wave wn holds 64 of each, so SwiGLU pairs inside the wave.
 //
 // A stage is 64 of K (two MX blocks).  Every wave issues its share of the
-// stage's asynchronous global->LDS loads (1 KB of codes, 4 x 1 KB of
-// activations, and every 8 stages, for waves 0-3, 1 KB of scales) two stages
-// ahead into a ring of three, then computes the current stage: one barrier
-// per stage.
+// stage's asynchronous global->LDS loads (1 KB of codes, 3 x 1 KB of
+// activations, and every 8 stages, for waves 0-3, 1 KB of scales) into a
+// ring of four.  Operands are read from LDS one stage ahead: in the
+// iteration that runs stage s's MFMAs the wave reads stage s+1's operands,
+// so LDS latency hides behind MFMAs; one barrier per stage.
 //
 // Register roles follow v_mfma_f32_16x16x32_bf16: weights are operand A
 // (row = weight row), activations operand B (row = token row).  In a stage,
@@ -40,30 +41,34 @@
 // LDS layouts are swizzled so that the MFMA waves' reads spread over the
 // banks: token row r keeps its 16-byte chunk c in slot c ^ (r & 7); weight
 // row r keeps its two 16-byte blocks swapped when bit 2 of r is set.
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace mxm {
 namespace {
 
-constexpr int kMT = 256;             // token rows per tile
+constexpr int kMT = 192;             // token rows per tile
 constexpr int kNT = 256;             // weight rows per tile
 constexpr int kKS = 64;              // K per stage (2 MX blocks)
-constexpr int kRing = 3;             // stages in the LDS ring
+constexpr int kRing = 4;             // stages in the LDS ring
 constexpr int kWaves = 8;
 constexpr int kDThreads = kWaves * kWave;
 constexpr int kMinRows = 64;         // experts with fewer rows use the streaming kernels
 constexpr int kMaxE = 1024;
 constexpr int kWB = kNT * kKS / 2;   // 8 KB of codes per stage
-constexpr int kAB = kMT * kKS * 2;   // 32 KB of activations per stage
+constexpr int kAB = kMT * kKS * 2;   // 24 KB of activations per stage
 constexpr int kStage = kWB + kAB;
 constexpr int kScStages = 8;         // stages per scale chunk (16 blocks = 16 B per row)
 constexpr int kSChunk = kNT * 16;    // 4 KB
 constexpr int kLdsS = kRing * kStage;
 constexpr int kLdsMpre = kLdsS + 2 * kSChunk;
 constexpr int kLdsBytes = kLdsMpre + (kMaxE + 4) * 4;
-constexpr int kLoadsPerStage = 5;    // per wave: 1 code and 4 activation loads
+constexpr int kActLoads = kAB / 1024 / kWaves;   // 3
+constexpr int kLoadsPerStage = 1 + kActLoads;     // per wave: 1 code and 3 activation loads
+constexpr int kMSub = kMT / 64;                   // token subtiles per wave (3)
 static_assert(kLdsBytes <= 160 * 1024, "LDS per CU");
-static_assert(kWB == kWaves * 1024 && kAB == 4 * kWaves * 1024 && kSChunk == 4 * 1024,
+static_assert(kWB == kWaves * 1024 && kAB == kActLoads * kWaves * 1024 && kSChunk == 4 * 1024,
               "every wave issues the same stage loads; waves 0-3 one scale load each");
 static_assert((kRing - 2) * kLoadsPerStage <= 63, "vmcnt range");
 
@@ -122,7 +127,7 @@ struct Item {
 };
 
 // One work item: K loop over the ring, then the epilogue.  NV = this wave's
-// valid token subtiles (wm, wm+4, ... below the tile's row count).
+// valid token subtiles (wm, wm+4, wm+8 below the tile's row count).
 template <bool GU, int NV>
 __device__ __forceinline__ void run_item(uint8_t* lds, const Item& it, int K, int I, int H, int k,
                                          const __amdgpu_buffer_rsrc_t& rs,
@@ -140,9 +145,9 @@ __device__ __forceinline__ void run_item(uint8_t* lds, const Item& it, int K, in
   // activations: loads j = wave + 8q cover tile rows 8j..8j+7; lane -> row
   // 8j + lane/8, slot lane%8 holding chunk (lane%8) ^ (row&7).  Rows past the
   // tile's end get 2^31 added: out of the buffer's range, no memory traffic.
-  uint32_t voff[4];
+  uint32_t voff[kActLoads];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < kActLoads; ++q) {
     const int tr = 8 * (wave + kWaves * q) + (lane >> 3);
     const int row = it.row0 + min(tr, it.rows - 1);
     const uint32_t src = GU ? uint32_t(sorted_pairs[row] / k) : uint32_t(row);
@@ -172,7 +177,7 @@ __device__ __forceinline__ void run_item(uint8_t* lds, const Item& it, int K, in
     uint8_t* st = lds + (s % kRing) * kStage;
     __builtin_amdgcn_global_load_lds(wsrc + s * 32, lds_at(st, 1024 * wave), 16, 0, 0);
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int q = 0; q < kActLoads; ++q)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds_at(st, kWB + 1024 * (wave + kWaves * q)),
                                                16, voff[q] + uint32_t(s * kKS * 2), 0, 0, 0);
   };
@@ -183,62 +188,30 @@ __device__ __forceinline__ void run_item(uint8_t* lds, const Item& it, int K, in
 #pragma unroll
     for (int i = 0; i < NV; ++i) acc[a][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // every subtile row's place in the stage
-  int wslot[8], srow[8];
+  // every subtile row's place in the stage: a base plus a constant per subtile
+  // (subtile rows are multiples of 16, so the swizzle bits come from r16)
+  const int wbase = 16 * (2 * r16 + ((g >> 1) ^ ((r16 >> 2) & 1))) + 8 * (g & 1);
+  const int sbase = 16 * r16 + (g >> 1);
+  int abase[2];
 #pragma unroll
-  for (int a = 0; a < 8; ++a) {
-    const int row = local_row<GU>(wn, a) + r16;
-    wslot[a] = 16 * (2 * row + ((g >> 1) ^ ((row >> 2) & 1))) + 8 * (g & 1);
-    srow[a] = 16 * row + (g >> 1);
-  }
-  int aoff[NV > 0 ? NV : 1][2];
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int tr = 16 * (wm + 4 * i) + r16;
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) aoff[i][kk] = tr * 128 + (((2 * g + kk) ^ (tr & 7)) * 16);
-  }
+  for (int kk = 0; kk < 2; ++kk) abase[kk] = (16 * wm + r16) * 128 + (((2 * g + kk) ^ (r16 & 7)) * 16);
 
-  // Issue order: chunk 0, stage 0, stage 1, then per iteration s the next
-  // stage s + 2, preceded every 8 stages (s % 8 == 0) by scale chunk s/8 + 1
-  // (the buffer of chunk s/8 - 1, whose last stage s - 1 is done).  nst is a
-  // multiple of 8.
-  static_assert(kRing == 3, "one stage in flight behind the current one");
-  issue_scales(0);
-  issue(0);
-  issue(1);
-  for (int s = 0; s < nst; ++s) {
-    // this wave's loads of stage s (and everything issued before) have landed;
-    // those issued after them (stage s + 1 and maybe a scale chunk) may still
-    // be on the way
-    if (s + 1 < nst) {
-      if (scl_wave && s % kScStages == 1 && s - 1 + kScStages < nst)
-        __builtin_amdgcn_s_waitcnt(MXM_VMCNT(kLoadsPerStage + 1));
-      else
-        __builtin_amdgcn_s_waitcnt(MXM_VMCNT(kLoadsPerStage));
-    } else {
-      __builtin_amdgcn_s_waitcnt(MXM_VMCNT(0));
-    }
-    __builtin_amdgcn_s_barrier();
-    if (s + kRing - 1 < nst) {
-      if (s % kScStages == 0 && s + kScStages < nst) issue_scales(s / kScStages + 1);
-      issue(s + kRing - 1);
-    }
+  // Activation operands of one stage, read from LDS one stage ahead of their
+  // MFMAs; codes and scale bytes are read at the top of the iteration that
+  // uses them, before its barrier.
+  typedef uint4 Acts[2][NV > 0 ? NV : 1];
+  auto read_acts = [&](int s, Acts& b) {
     if constexpr (NV > 0) {
-      const uint8_t* st = lds + (s % kRing) * kStage;
-      uint2 cw[8];
-      uint32_t sb[8];
-#pragma unroll
-      for (int a = 0; a < 8; ++a) {
-        cw[a] = *reinterpret_cast<const uint2*>(st + wslot[a]);
-        sb[a] = lds[kLdsS + ((s / kScStages) & 1) * kSChunk + srow[a] + 2 * (s % kScStages)];
-      }
-      uint4 b[2][NV];
+      const uint8_t* st = lds + (s % kRing) * kStage + kWB;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
         for (int i = 0; i < NV; ++i)
-          b[kk][i] = *reinterpret_cast<const uint4*>(st + kWB + aoff[i][kk]);
+          b[kk][i] = *reinterpret_cast<const uint4*>(st + abase[kk] + 64 * 128 * i);
+    }
+  };
+  auto compute = [&](const uint2 (&cw)[8], const uint32_t (&sb)[8], const Acts& b) {
+    if constexpr (NV > 0) {
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
@@ -246,11 +219,74 @@ __device__ __forceinline__ void run_item(uint8_t* lds, const Item& it, int K, in
           const bf16x8 wa = dequant8(kk ? cw[a].y : cw[a].x, e8m0_to_f32(sb[a]));
 #pragma unroll
           for (int i = 0; i < NV; ++i)
-            acc[a][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, as_bf16x8(b[kk][i]), acc[a][i],
-                                                                0, 0, 0);
+            acc[a][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, as_bf16x8(b[kk][i]),
+                                                                acc[a][i], 0, 0, 0);
         }
     }
+  };
+
+  // Pipeline.  Iteration s: read stage s's codes and scale bytes (landed at
+  // barrier s); wait until stage s + 1 has landed; barrier; issue stage s + 3
+  // into the slot of stage s - 1 (every wave finished it in iteration s - 1);
+  // read stage s + 1's activations; run stage s's MFMAs while they fly.
+  // Issue order: chunk 0, stages 0..2; then per iteration s scale chunk
+  // s/8 + 1 when s % 8 == 0 (its buffer held chunk s/8 - 1, whose last
+  // reader, iteration s - 1, came before barrier s + 1), then stage s + 3.
+  // nst is a multiple of 8.
+  static_assert(kRing == 4, "stages s - 1 .. s + 2 in the ring while s + 3 loads");
+  issue_scales(0);
+#pragma unroll
+  for (int p = 0; p < kRing - 1; ++p) issue(p);
+  __builtin_amdgcn_s_waitcnt(MXM_VMCNT(2 * kLoadsPerStage));    // chunk 0, stage 0
+  wg_barrier();
+  // a scale chunk went out in iteration i (before stage i + 3)
+  auto chunk_at = [&](int i) { return scl_wave && i >= 0 && i % kScStages == 0 && i + kScStages < nst; };
+  Acts ba, bb;
+  read_acts(0, ba);
+  // one iteration; PREFETCH (a stage s + 1 exists) is false only for the
+  // last stage, so the loop body is straight-line code and the compiler's
+  // LDS counter waits stay exact
+  auto step = [&](auto prefetch, int s, Acts& cur, Acts& nxt) {
+    constexpr bool PREFETCH = decltype(prefetch)::value;
+    uint2 cw[8];
+    uint32_t sb[8];
+    if constexpr (NV > 0) {
+      const uint8_t* st = lds + (s % kRing) * kStage;
+      const uint8_t* sc = lds + kLdsS + ((s / kScStages) & 1) * kSChunk + 2 * (s % kScStages);
+#pragma unroll
+      for (int a = 0; a < 8; ++a) {
+        const int lr = local_row<GU>(wn, a);
+        cw[a] = *reinterpret_cast<const uint2*>(st + wbase + 32 * lr);
+        sb[a] = sc[sbase + 16 * lr];
+      }
+    }
+    if constexpr (PREFETCH) {
+      // issued after stage s + 1 (in iteration s - 2): stage s + 2 and the
+      // chunk of iteration s - 1
+      if (s + 2 < nst) {
+        if (chunk_at(s - 1)) __builtin_amdgcn_s_waitcnt(MXM_VMCNT(kLoadsPerStage + 1));
+        else __builtin_amdgcn_s_waitcnt(MXM_VMCNT(kLoadsPerStage));
+      } else {
+        __builtin_amdgcn_s_waitcnt(MXM_VMCNT(0));
+      }
+      wg_barrier();
+      if (s + kRing - 1 < nst) {
+        if (chunk_at(s)) issue_scales(s / kScStages + 1);
+        issue(s + kRing - 1);
+      }
+      read_acts(s + 1, nxt);
+    }
+    compute(cw, sb, cur);
+  };
+  using yes = std::integral_constant<bool, true>;
+  using no = std::integral_constant<bool, false>;
+  int s = 0;
+  for (; s + 2 < nst; s += 2) {
+    step(yes(), s, ba, bb);
+    step(yes(), s + 1, bb, ba);
   }
+  step(yes(), s, ba, bb);            // nst is even: stages nst - 2 and nst - 1
+  step(no(), s + 1, bb, ba);
 
   // epilogue: lane holds D[4g+v][r16]: weight row 4g+v of subtile a, token
   // row r16 of subtile wm + 2i
@@ -333,9 +369,8 @@ __global__ __launch_bounds__(kDThreads, 1) void k_dense(
     it.row0 = __builtin_amdgcn_readfirstlane(off0 + m * kMT);
     it.rows = __builtin_amdgcn_readfirstlane(min(kMT, offsets[e + 1] - off0 - m * kMT));
     const int nsub = (it.rows + 15) >> 4;
-    const int nv = __builtin_amdgcn_readfirstlane(max(0, min(4, (nsub - wm + 3) >> 2)));
+    const int nv = __builtin_amdgcn_readfirstlane(max(0, min(kMSub, (nsub - wm + 3) >> 2)));
     switch (nv) {
-      case 4: run_item<GU, 4>(lds, it, K, I, H, k, rs, sorted_pairs, codes, scales, out); break;
       case 3: run_item<GU, 3>(lds, it, K, I, H, k, rs, sorted_pairs, codes, scales, out); break;
       case 2: run_item<GU, 2>(lds, it, K, I, H, k, rs, sorted_pairs, codes, scales, out); break;
       case 1: run_item<GU, 1>(lds, it, K, I, H, k, rs, sorted_pairs, codes, scales, out); break;
