@@ -9,35 +9,53 @@
 namespace mxm {
 namespace {
 
+// One workgroup per (token, 1024 columns): the token's k rows and weights are
+// read once into LDS, then every thread issues its k row loads together (no
+// branch between them: a dropped pair reads row 0 and its term is not added)
+// and accumulates them in slot order.
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y,
                                                  const float* __restrict__ w,
                                                  const int32_t* __restrict__ pair_to_row, int T,
                                                  int H, int k, float* __restrict__ out) {
-  const int q = H >> 2;                                   // float4 columns per token
-  const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (idx >= int64_t(T) * q) return;
-  const int64_t t = idx / q;
-  const int c = int(idx - t * q) * 4;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int j = 0; j < k; ++j) {
-    const int r = pair_to_row[t * k + j];
-    if (r < 0) continue;
-    const float wj = w[t * k + j];
-    const float4 v = *reinterpret_cast<const float4*>(y + int64_t(r) * H + c);
-    acc.x = fmaf(wj, v.x, acc.x);
-    acc.y = fmaf(wj, v.y, acc.y);
-    acc.z = fmaf(wj, v.z, acc.z);
-    acc.w = fmaf(wj, v.w, acc.w);
+  __shared__ int32_t srow[32];
+  __shared__ float sw[32];
+  const int t = blockIdx.x;
+  if (threadIdx.x < k) {
+    srow[threadIdx.x] = pair_to_row[int64_t(t) * k + threadIdx.x];
+    sw[threadIdx.x] = w[int64_t(t) * k + threadIdx.x];
   }
-  *reinterpret_cast<float4*>(out + t * H + c) = acc;
+  __syncthreads();
+  const int c = blockIdx.y * 1024 + threadIdx.x * 4;
+  if (c >= H) return;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j0 = 0; j0 < k; j0 += 8) {
+    float4 v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = (j0 + i < k) ? max(srow[j0 + i], 0) : 0;
+      v[i] = *reinterpret_cast<const float4*>(y + int64_t(r) * H + c);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int j = j0 + i;
+      if (j < k && srow[j] >= 0) {
+        const float wj = sw[j];
+        acc.x = fmaf(wj, v[i].x, acc.x);
+        acc.y = fmaf(wj, v[i].y, acc.y);
+        acc.z = fmaf(wj, v[i].z, acc.z);
+        acc.w = fmaf(wj, v[i].w, acc.w);
+      }
+    }
+  }
+  *reinterpret_cast<float4*>(out + int64_t(t) * H + c) = acc;
 }
 
 }  // namespace
 
 hipError_t launch_combine(const float* y, const float* w, const int32_t* pair_to_row, int T,
                           int H, int k, float* out, hipStream_t s) {
-  const int64_t n = int64_t(T) * (H / 4);
-  k_combine<<<dim3(unsigned((n + 255) / 256)), 256, 0, s>>>(y, w, pair_to_row, T, H, k, out);
+  k_combine<<<dim3(unsigned(T), unsigned((H + 1023) / 1024)), 256, 0, s>>>(y, w, pair_to_row, T,
+                                                                          H, k, out);
   return hipGetLastError();
 }
 

@@ -9,9 +9,11 @@
 //
 // Work decomposition
 //   * Each expert's rows (a segment of the permutation) are cut into tiles of
-//     up to MT = 16*MS rows.  The grid is sized on the host from T, k and E
-//     only (an upper bound on the tile count); each workgroup finds its tile
-//     from the device-side offsets and leaves if past the last one.  Nothing
+//     up to MT = 16*MS rows.  The host bounds the tile count from T, k and E
+//     only; each workgroup walks tile slots grid-stride, finds each tile from
+//     the device-side offsets and stops at the first slot past the last tile
+//     (the grid is capped, so a bound far above the real count, as when most
+//     rows go to the dense kernel, costs few empty workgroups).  Nothing
 //     waits on the host.
 //   * A workgroup has 4 waves; each wave owns NSUB 16-row subtiles of output
 //     features and streams the matching weight rows over the whole K.
@@ -178,12 +180,13 @@ __global__ __launch_bounds__(kThreads) void k_gate_up(
   const int lane = lane_id();
   const int r16 = lane & 15;
   const int g = lane >> 4;
-  const int slot = blockIdx.x / ntile_n;
-  const int nt = blockIdx.x - slot * ntile_n;
+  for (int idx = blockIdx.x;; idx += gridDim.x) {
+  const int slot = idx / ntile_n;
+  const int nt = idx - slot * ntile_n;
   Tile t;
   if (!find_tile(offsets, E, 16 * MS, slot, t, 1, hi)) return;
   const int i0 = (nt * kWaves + wave) * 16 * NSUB;
-  if (i0 >= I) return;
+  if (i0 >= I) continue;
 
   const int nblk = H / 32;
   const size_t erow = size_t(t.e) * 2 * I;
@@ -235,6 +238,7 @@ __global__ __launch_bounds__(kThreads) void k_gate_up(
       *dst = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
     }
   }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -249,12 +253,13 @@ __global__ __launch_bounds__(kThreads) void k_down(
   const int lane = lane_id();
   const int r16 = lane & 15;
   const int g = lane >> 4;
-  const int slot = blockIdx.x / ntile_n;
-  const int nt = blockIdx.x - slot * ntile_n;
+  for (int idx = blockIdx.x;; idx += gridDim.x) {
+  const int slot = idx / ntile_n;
+  const int nt = idx - slot * ntile_n;
   Tile t;
   if (!find_tile(offsets, E, 16 * MS, slot, t, 1, hi)) return;
   const int n0 = (nt * kWaves + wave) * 16 * NSUB;
-  if (n0 >= H) return;
+  if (n0 >= H) continue;
 
   const int nblk = I / 32;
   const size_t erow = size_t(t.e) * H;
@@ -296,6 +301,7 @@ __global__ __launch_bounds__(kThreads) void k_down(
       *dst = make_float4(v[0], v[1], v[2], v[3]);
     }
   }
+  }
 }
 
 // Rows per tile: MS subtiles of 16.  Chosen from the mean rows per touched
@@ -310,6 +316,24 @@ int choose_ms(int R, int E) {
 
 int tile_slots(int R, int E, int mt) { return (R < E ? R : E) + (R + mt - 1) / mt; }
 
+int stream_cus() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v < 1)
+      v = 256;
+    n = v;
+  }
+  return n;
+}
+
+// workgroups launched: the tile-slot bound, capped at a few per CU
+unsigned stream_grid(int64_t slots_times_n) {
+  const int64_t cap = int64_t(4) * stream_cus();
+  return unsigned(slots_times_n < cap ? slots_times_n : cap);
+}
+
 template <int MS>
 hipError_t gate_up_ms(const uint16_t* x, const int32_t* sp, const int32_t* off, int T, int H,
                       int I, int E, int k, const uint8_t* c, const uint8_t* sc, uint16_t* h,
@@ -317,9 +341,9 @@ hipError_t gate_up_ms(const uint16_t* x, const int32_t* sp, const int32_t* off, 
   constexpr int NSUB = MXM_GU_NSUB;
   const int R = T * k;
   const int ntile_n = (I + kWaves * 16 * NSUB - 1) / (kWaves * 16 * NSUB);
-  const int64_t grid = int64_t(tile_slots(R, E, 16 * MS)) * ntile_n;
+  const unsigned grid = stream_grid(int64_t(tile_slots(R, E, 16 * MS)) * ntile_n);
   const size_t lds = size_t(kWaves) * 2 * NSUB * 16 * (H / 32);
-  k_gate_up<MS, NSUB><<<dim3(unsigned(grid)), kThreads, lds, s>>>(x, sp, off, H, I, E, k, c, sc,
+  k_gate_up<MS, NSUB><<<dim3(grid), kThreads, lds, s>>>(x, sp, off, H, I, E, k, c, sc,
                                                                     h, ntile_n, hi);
   return hipGetLastError();
 }
@@ -330,9 +354,9 @@ hipError_t down_ms(const uint16_t* h, const int32_t* off, int T, int H, int I, i
   constexpr int NSUB = MXM_DN_NSUB;
   const int R = T * k;
   const int ntile_n = (H + kWaves * 16 * NSUB - 1) / (kWaves * 16 * NSUB);
-  const int64_t grid = int64_t(tile_slots(R, E, 16 * MS)) * ntile_n;
+  const unsigned grid = stream_grid(int64_t(tile_slots(R, E, 16 * MS)) * ntile_n);
   const size_t lds = size_t(kWaves) * NSUB * 16 * (I / 32);
-  k_down<MS, NSUB><<<dim3(unsigned(grid)), kThreads, lds, s>>>(h, off, H, I, E, c, sc, y, ntile_n,
+  k_down<MS, NSUB><<<dim3(grid), kThreads, lds, s>>>(h, off, H, I, E, c, sc, y, ntile_n,
                                                                hi);
   return hipGetLastError();
 }

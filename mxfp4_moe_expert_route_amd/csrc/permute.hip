@@ -8,19 +8,21 @@
 // Ids outside [0, E) are dropped (pair_to_row = -1, not counted) so that bad
 // input cannot send a store out of bounds.
 //
-// One workgroup of 8 waves.  Wave w owns a contiguous range of pairs.
+// One workgroup of 16 waves.  Wave w owns a contiguous range of pairs.
 //  1. per-wave histograms in LDS (integer atomics: order-free, deterministic)
 //  2. per-expert exclusive bases across waves, block scan over experts
 //  3. each wave walks its range 64 pairs at a time; a pair's rank among the
 //     earlier pairs of its expert in the same 64 comes from a ballot-based
 //     match (one ballot per bit of the expert id), so the scatter is stable
-//     without sorting.
+//     without sorting.  The ids of 8 such groups are loaded at once, so the
+//     walk pays one memory latency per 512 pairs.
 #include "common.hpp"
 
 namespace mxm {
 namespace {
 
-constexpr int kPermWaves = 8;
+constexpr int kPermWaves = 16;
+constexpr int kBatch = 8;                     // 64-pair groups whose ids load together
 constexpr int kPermThreads = kPermWaves * kWave;
 
 __global__ __launch_bounds__(kPermThreads) void k_permute(const int32_t* __restrict__ ids, int R,
@@ -94,24 +96,32 @@ __global__ __launch_bounds__(kPermThreads) void k_permute(const int32_t* __restr
   // 3. stable scatter; my_hist[e] is the next free row of expert e for this wave
   const int nbits = (E > 1) ? 32 - __clz(E - 1) : 0;
   const unsigned long long lt = (1ull << lane) - 1ull;
-  for (int c = beg; c < end; c += kWave) {
-    const int p = c + lane;
-    const int raw = (p < end) ? ids[p] : 0;
-    const bool valid = (p < end) && unsigned(raw) < unsigned(E);
-    const int key = valid ? raw : 0;
-    if (p < end && !valid) pair_to_row[p] = -1;   // out-of-range id: pair dropped
-    unsigned long long m = __ballot(valid);
-    for (int b = 0; b < nbits; ++b) {
-      const bool bit = (key >> b) & 1;
-      const unsigned long long bb = __ballot(valid && bit);
-      m &= bit ? bb : ~bb;
+  for (int c0 = beg; c0 < end; c0 += kBatch * kWave) {
+    int raw[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int p = c0 + i * kWave + lane;
+      raw[i] = (p < end) ? ids[p] : 0;
     }
-    if (valid) {
-      const int rank = __popcll(m & lt);
-      const int pos = my_hist[key] + rank;
-      sorted_pairs[pos] = p;
-      pair_to_row[p] = pos;
-      if ((m >> lane) == 1ull) my_hist[key] += __popcll(m);   // last lane of its expert
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int p = c0 + i * kWave + lane;
+      const bool valid = (p < end) && unsigned(raw[i]) < unsigned(E);
+      const int key = valid ? raw[i] : 0;
+      if (p < end && !valid) pair_to_row[p] = -1;   // out-of-range id: pair dropped
+      unsigned long long m = __ballot(valid);
+      for (int b = 0; b < nbits; ++b) {
+        const bool bit = (key >> b) & 1;
+        const unsigned long long bb = __ballot(valid && bit);
+        m &= bit ? bb : ~bb;
+      }
+      if (valid) {
+        const int rank = __popcll(m & lt);
+        const int pos = my_hist[key] + rank;
+        sorted_pairs[pos] = p;
+        pair_to_row[p] = pos;
+        if ((m >> lane) == 1ull) my_hist[key] += __popcll(m);   // last lane of its expert
+      }
     }
   }
 }
@@ -123,6 +133,14 @@ hipError_t launch_permute(const int32_t* ids, int T, int E, int k, int32_t* coun
                           hipStream_t s) {
   const int R = T * k;
   const size_t lds = size_t(kPermWaves + 1) * E * sizeof(int32_t);
+  static bool attr_set = false;
+  if (!attr_set) {                // E up to 1024: more than the default 64 KB
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_permute),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             int((kPermWaves + 1) * 1024 * sizeof(int32_t)));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
   k_permute<<<1, kPermThreads, lds, s>>>(ids, R, E, counts, offsets, sorted_pairs, pair_to_row);
   return hipGetLastError();
 }
