@@ -20,11 +20,14 @@
 // line) of each token row; the scale bytes of a row arrive 16 at a time (8
 // stages' worth) in a separate chunk buffer.
 //
-// Workgroup: 8 waves in a 2 x 4 grid, two per SIMD; wave (wn, wm) computes
-// 128 weight rows (8 subtiles of 16) x 48 token rows (the 16-row subtiles wm,
-// wm+4, wm+8 of the tile), 96 fp32 accumulators per lane.  For gate/up the
+// Workgroup: 8 waves in a 4 x 2 grid, two per SIMD; wave (wn, wm) computes
+// 64 weight rows (4 subtiles of 16) x 96 token rows (the 16-row subtiles wm,
+// wm+2, ..., wm+10 of the tile), 96 fp32 accumulators per lane.  Each weight
+// row is dequantised by the two waves that share it, and each dequantised
+// operand feeds six MFMAs: the FP4 conversion runs at half the VALU rate, so
+// conversions per MFMA, not LDS bytes, set this split.  For gate/up the
 // workgroup's 256 weight rows are 128 gate columns and the same 128 up
-// columns; wave wn holds 64 of each, so SwiGLU pairs inside the wave.
+// columns; wave wn holds 32 of each, so SwiGLU pairs inside the wave.
 //
 // A stage is 64 of K (two MX blocks).  Every wave issues its share of the
 // stage's asynchronous global->LDS loads (1 KB of codes, 3 x 1 KB of
@@ -38,9 +41,14 @@
 // lane group g covers K elements 16g..16g+15 (half of MX block g/2), MFMA kk
 // the 8 from 16g+8kk; weights and activations use the same assignment.
 //
-// LDS layouts are swizzled so that the MFMA waves' reads spread over the
-// banks: token row r keeps its 16-byte chunk c in slot c ^ (r & 7); weight
-// row r keeps its two 16-byte blocks swapped when bit 2 of r is set.
+// LDS layouts are chosen for the MFMA waves' reads.  Activations are stored
+// in 1 KB blocks, one per (16-row subtile, MFMA kk): lane l = 16g + r of the
+// read finds its 16 bytes (row r, K chunk 2g + kk) at 16 l, so every operand
+// read is one contiguous 1 KB; the load that fills a block fetches those 64
+// pieces (half of each of 16 rows' 128 bytes).  Row-strided layouts, even
+// xor-swizzled ones, read at about half that rate on gfx950.  Weight rows are
+// 32 bytes; row r keeps its two 16-byte blocks swapped when bit 3 of r is
+// set, which makes the 8-byte code reads conflict-free.
 #include <type_traits>
 
 #include "common.hpp"
@@ -66,7 +74,10 @@ constexpr int kLdsMpre = kLdsS + 2 * kSChunk;
 constexpr int kLdsBytes = kLdsMpre + (kMaxE + 4) * 4;
 constexpr int kActLoads = kAB / 1024 / kWaves;   // 3
 constexpr int kLoadsPerStage = 1 + kActLoads;     // per wave: 1 code and 3 activation loads
-constexpr int kMSub = kMT / 64;                   // token subtiles per wave (3)
+constexpr int kWN = 4;                            // waves along weight rows
+constexpr int kWM = kWaves / kWN;                 // waves along token rows (2)
+constexpr int kASub = kNT / kWN / 16;             // weight subtiles per wave (4)
+constexpr int kMSub = kMT / 16 / kWM;             // token subtiles per wave (6)
 static_assert(kLdsBytes <= 160 * 1024, "LDS per CU");
 static_assert(kWB == kWaves * 1024 && kAB == kActLoads * kWaves * 1024 && kSChunk == 4 * 1024,
               "every wave issues the same stage loads; waves 0-3 one scale load each");
@@ -107,11 +118,13 @@ __device__ __forceinline__ int expert_of(const int* mpre, int E, int tau) {
   return lo;
 }
 
-// Local weight row (0..255 within the n-tile) of subtile a of wave wn.
+// Local weight row (0..255 within the n-tile) of subtile a of wave wn: gate
+// subtiles first, then the up subtiles of the same columns.
 template <bool GU>
 __device__ __forceinline__ int local_row(int wn, int a) {
-  if constexpr (GU) return a < 4 ? 64 * wn + 16 * a : 128 + 64 * wn + 16 * (a - 4);
-  else return 128 * wn + 16 * a;
+  constexpr int h = kASub / 2;
+  if constexpr (GU) return a < h ? 16 * h * wn + 16 * a : 128 + 16 * h * wn + 16 * (a - h);
+  else return 16 * kASub * wn + 16 * a;
 }
 
 // Row in the whole weight tensor of local row r of n-tile n of expert e:
@@ -127,7 +140,7 @@ struct Item {
 };
 
 // One work item: K loop over the ring, then the epilogue.  NV = this wave's
-// valid token subtiles (wm, wm+4, wm+8 below the tile's row count).
+// valid token subtiles (wm, wm+2, ... below the tile's row count).
 template <bool GU, int NV>
 __device__ __forceinline__ void run_item(uint8_t* lds, const Item& it, int K, int I, int H, int k,
                                          const __amdgpu_buffer_rsrc_t& rs,
@@ -137,29 +150,31 @@ __device__ __forceinline__ void run_item(uint8_t* lds, const Item& it, int K, in
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = lane_id();
   const int r16 = lane & 15, g = lane >> 4;
-  const int wn = wave & 1, wm = wave >> 1;
+  const int wn = wave % kWN, wm = wave / kWN;
   const int nst = K / kKS;
   const int nblk = K / 32;
 
   // ---- this lane's load sources
-  // activations: loads j = wave + 8q cover tile rows 8j..8j+7; lane -> row
-  // 8j + lane/8, slot lane%8 holding chunk (lane%8) ^ (row&7).  Rows past the
-  // tile's end get 2^31 added: out of the buffer's range, no memory traffic.
+  // activations: load j = wave + 8q fills the block of subtile j/2, MFMA
+  // kk = j%2: lane 16g + r fetches tile row 16(j/2) + r, K chunk 2g + kk.
+  // Rows past the tile's end get 2^31 added: out of the buffer's range, no
+  // memory traffic.
   uint32_t voff[kActLoads];
 #pragma unroll
   for (int q = 0; q < kActLoads; ++q) {
-    const int tr = 8 * (wave + kWaves * q) + (lane >> 3);
+    const int j = wave + kWaves * q;
+    const int tr = 16 * (j >> 1) + r16;
     const int row = it.row0 + min(tr, it.rows - 1);
     const uint32_t src = GU ? uint32_t(sorted_pairs[row] / k) : uint32_t(row);
-    voff[q] = src * uint32_t(K * 2) + uint32_t((((lane & 7) ^ (tr & 7))) * 16) +
+    voff[q] = src * uint32_t(K * 2) + uint32_t((2 * g + (j & 1)) * 16) +
               (uint32_t(tr >= it.rows) << 31);
   }
   // codes: load i = wave covers local rows 32i..32i+31; lane -> row
-  // 32i + lane/2, slot parity lane&1 holding block (lane&1) ^ ((row>>2)&1)
+  // 32i + lane/2, slot parity lane&1 holding block (lane&1) ^ ((row>>3)&1)
   const uint8_t* wsrc;
   {
     const int r = 32 * wave + (lane >> 1);
-    const int b = (lane & 1) ^ ((r >> 2) & 1);
+    const int b = (lane & 1) ^ ((r >> 3) & 1);
     wsrc = codes + weight_row<GU>(it.e, it.n, r, I, H) * (K / 2) + b * 16;
   }
   // scales (waves 0-3): local rows 64 wave + lane, 16 bytes (8 stages) each
@@ -182,19 +197,19 @@ __device__ __forceinline__ void run_item(uint8_t* lds, const Item& it, int K, in
                                                16, voff[q] + uint32_t(s * kKS * 2), 0, 0, 0);
   };
 
-  f32x4 acc[8][NV > 0 ? NV : 1];
+  f32x4 acc[kASub][NV > 0 ? NV : 1];
 #pragma unroll
-  for (int a = 0; a < 8; ++a)
+  for (int a = 0; a < kASub; ++a)
 #pragma unroll
     for (int i = 0; i < NV; ++i) acc[a][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // every subtile row's place in the stage: a base plus a constant per subtile
   // (subtile rows are multiples of 16, so the swizzle bits come from r16)
-  const int wbase = 16 * (2 * r16 + ((g >> 1) ^ ((r16 >> 2) & 1))) + 8 * (g & 1);
+  const int wbase = 16 * (2 * r16 + ((g >> 1) ^ ((r16 >> 3) & 1))) + 8 * (g & 1);
   const int sbase = 16 * r16 + (g >> 1);
   int abase[2];
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk) abase[kk] = (16 * wm + r16) * 128 + (((2 * g + kk) ^ (r16 & 7)) * 16);
+  for (int kk = 0; kk < 2; ++kk) abase[kk] = 1024 * (2 * wm + kk) + 16 * lane;
 
   // Activation operands of one stage, read from LDS one stage ahead of their
   // MFMAs; codes and scale bytes are read at the top of the iteration that
@@ -207,15 +222,15 @@ __device__ __forceinline__ void run_item(uint8_t* lds, const Item& it, int K, in
       for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
         for (int i = 0; i < NV; ++i)
-          b[kk][i] = *reinterpret_cast<const uint4*>(st + abase[kk] + 64 * 128 * i);
+          b[kk][i] = *reinterpret_cast<const uint4*>(st + abase[kk] + 2048 * kWM * i);
     }
   };
-  auto compute = [&](const uint2 (&cw)[8], const uint32_t (&sb)[8], const Acts& b) {
+  auto compute = [&](const uint2 (&cw)[kASub], const uint32_t (&sb)[kASub], const Acts& b) {
     if constexpr (NV > 0) {
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-        for (int a = 0; a < 8; ++a) {
+        for (int a = 0; a < kASub; ++a) {
           const bf16x8 wa = dequant8(kk ? cw[a].y : cw[a].x, e8m0_to_f32(sb[a]));
 #pragma unroll
           for (int i = 0; i < NV; ++i)
@@ -248,13 +263,13 @@ __device__ __forceinline__ void run_item(uint8_t* lds, const Item& it, int K, in
   // LDS counter waits stay exact
   auto step = [&](auto prefetch, int s, Acts& cur, Acts& nxt) {
     constexpr bool PREFETCH = decltype(prefetch)::value;
-    uint2 cw[8];
-    uint32_t sb[8];
+    uint2 cw[kASub];
+    uint32_t sb[kASub];
     if constexpr (NV > 0) {
       const uint8_t* st = lds + (s % kRing) * kStage;
       const uint8_t* sc = lds + kLdsS + ((s / kScStages) & 1) * kSChunk + 2 * (s % kScStages);
 #pragma unroll
-      for (int a = 0; a < 8; ++a) {
+      for (int a = 0; a < kASub; ++a) {
         const int lr = local_row<GU>(wn, a);
         cw[a] = *reinterpret_cast<const uint2*>(st + wbase + 32 * lr);
         sb[a] = sc[sbase + 16 * lr];
@@ -289,32 +304,32 @@ __device__ __forceinline__ void run_item(uint8_t* lds, const Item& it, int K, in
   step(no(), s + 1, bb, ba);
 
   // epilogue: lane holds D[4g+v][r16]: weight row 4g+v of subtile a, token
-  // row r16 of subtile wm + 2i
+  // row r16 of subtile wm + kWM i
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
-    const int m = 16 * (wm + 4 * i) + r16;
+    const int m = 16 * (wm + kWM * i) + r16;
     if (m >= it.rows) continue;
     const size_t row = size_t(it.row0 + m);
     if constexpr (GU) {
       uint16_t* h = static_cast<uint16_t*>(out);
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
+      for (int a = 0; a < kASub / 2; ++a) {
         const f32x4 gv = acc[a][i];
-        const f32x4 uv = acc[a + 4][i];
+        const f32x4 uv = acc[a + kASub / 2][i];
         uint32_t hv[4];
 #pragma unroll
         for (int v = 0; v < 4; ++v)
           hv[v] = f32_to_bf16_rne(gv[v] / (1.0f + __expf(-gv[v])) * uv[v]);
-        const int col = 128 * it.n + 64 * wn + 16 * a + 4 * g;
+        const int col = 128 * it.n + 8 * kASub * wn + 16 * a + 4 * g;
         *reinterpret_cast<uint2*>(h + row * I + col) =
             make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
       }
     } else {
       float* y = static_cast<float*>(out);
 #pragma unroll
-      for (int a = 0; a < 8; ++a) {
+      for (int a = 0; a < kASub; ++a) {
         const f32x4 v = acc[a][i];
-        const int col = kNT * it.n + 128 * wn + 16 * a + 4 * g;
+        const int col = kNT * it.n + 16 * kASub * wn + 16 * a + 4 * g;
         *reinterpret_cast<float4*>(y + row * H + col) = make_float4(v[0], v[1], v[2], v[3]);
       }
     }
@@ -330,7 +345,7 @@ __global__ __launch_bounds__(kDThreads, 1) void k_dense(
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = lane_id();
-  const int wm = wave >> 1;
+  const int wm = wave / kWN;
   int* mpre = reinterpret_cast<int*>(lds + kLdsMpre);
   const int ntn = GU ? 2 * I / kNT : H / kNT;       // n-tiles per expert
 
@@ -369,8 +384,12 @@ __global__ __launch_bounds__(kDThreads, 1) void k_dense(
     it.row0 = __builtin_amdgcn_readfirstlane(off0 + m * kMT);
     it.rows = __builtin_amdgcn_readfirstlane(min(kMT, offsets[e + 1] - off0 - m * kMT));
     const int nsub = (it.rows + 15) >> 4;
-    const int nv = __builtin_amdgcn_readfirstlane(max(0, min(kMSub, (nsub - wm + 3) >> 2)));
+    const int nv =
+        __builtin_amdgcn_readfirstlane(max(0, min(kMSub, (nsub - wm + kWM - 1) / kWM)));
     switch (nv) {
+      case 6: run_item<GU, 6>(lds, it, K, I, H, k, rs, sorted_pairs, codes, scales, out); break;
+      case 5: run_item<GU, 5>(lds, it, K, I, H, k, rs, sorted_pairs, codes, scales, out); break;
+      case 4: run_item<GU, 4>(lds, it, K, I, H, k, rs, sorted_pairs, codes, scales, out); break;
       case 3: run_item<GU, 3>(lds, it, K, I, H, k, rs, sorted_pairs, codes, scales, out); break;
       case 2: run_item<GU, 2>(lds, it, K, I, H, k, rs, sorted_pairs, codes, scales, out); break;
       case 1: run_item<GU, 1>(lds, it, K, I, H, k, rs, sorted_pairs, codes, scales, out); break;
