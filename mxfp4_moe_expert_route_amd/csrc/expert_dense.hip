@@ -188,13 +188,19 @@ __device__ __forceinline__ void run_item(uint8_t* lds, const Item& it, int K, in
                                        lds_at(lds, kLdsS + (c & 1) * kSChunk + 1024 * wave), 16,
                                        0, 0);
   };
-  auto issue = [&](int s) {
+  // load q of stage s: q = 0 the codes, q = 1.. the activation blocks
+  auto issue_one = [&](int s, int q) {
     uint8_t* st = lds + (s % kRing) * kStage;
-    __builtin_amdgcn_global_load_lds(wsrc + s * 32, lds_at(st, 1024 * wave), 16, 0, 0);
+    if (q == 0)
+      __builtin_amdgcn_global_load_lds(wsrc + s * 32, lds_at(st, 1024 * wave), 16, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, lds_at(st, kWB + 1024 * (wave + kWaves * (q - 1))), 16,
+          voff[q - 1] + uint32_t(s * kKS * 2), 0, 0, 0);
+  };
+  auto issue = [&](int s) {
 #pragma unroll
-    for (int q = 0; q < kActLoads; ++q)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds_at(st, kWB + 1024 * (wave + kWaves * q)),
-                                               16, voff[q] + uint32_t(s * kKS * 2), 0, 0, 0);
+    for (int q = 0; q < kLoadsPerStage; ++q) issue_one(s, q);
   };
 
   f32x4 acc[kASub][NV > 0 ? NV : 1];
@@ -215,35 +221,44 @@ __device__ __forceinline__ void run_item(uint8_t* lds, const Item& it, int K, in
   // MFMAs; codes and scale bytes are read at the top of the iteration that
   // uses them, before its barrier.
   typedef uint4 Acts[2][NV > 0 ? NV : 1];
-  auto read_acts = [&](int s, Acts& b) {
+  auto read_acts = [&](int s, int kk, Acts& b) {
     if constexpr (NV > 0) {
       const uint8_t* st = lds + (s % kRing) * kStage + kWB;
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int i = 0; i < NV; ++i)
-          b[kk][i] = *reinterpret_cast<const uint4*>(st + abase[kk] + 2048 * kWM * i);
+      for (int i = 0; i < NV; ++i)
+        b[kk][i] = *reinterpret_cast<const uint4*>(st + abase[kk] + 2048 * kWM * i);
     }
   };
-  auto compute = [&](const uint2 (&cw)[kASub], const uint32_t (&sb)[kASub], const Acts& b) {
-    if constexpr (NV > 0) {
+  // hook(j) runs before the j-th group of MFMAs (one dequantised operand
+  // each), done(kk) after the MFMAs of half kk, whose activation registers
+  // are then free for the next stage's.  A wave without token rows (NV = 0)
+  // still runs the hooks: its share of the stage loads is issued there.
+  auto compute = [&](const uint2 (&cw)[kASub], const uint32_t (&sb)[kASub], const Acts& b,
+                     auto&& hook, auto&& done) {
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
+    for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
-        for (int a = 0; a < kASub; ++a) {
+      for (int a = 0; a < kASub; ++a) {
+        hook(kk * kASub + a);
+        if constexpr (NV > 0) {
           const bf16x8 wa = dequant8(kk ? cw[a].y : cw[a].x, e8m0_to_f32(sb[a]));
 #pragma unroll
           for (int i = 0; i < NV; ++i)
             acc[a][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, as_bf16x8(b[kk][i]),
                                                                 acc[a][i], 0, 0, 0);
         }
+      }
+      done(kk);
     }
   };
 
   // Pipeline.  Iteration s: read stage s's codes and scale bytes (landed at
-  // barrier s); wait until stage s + 1 has landed; barrier; issue stage s + 3
-  // into the slot of stage s - 1 (every wave finished it in iteration s - 1);
-  // read stage s + 1's activations; run stage s's MFMAs while they fly.
+  // barrier s); wait until stage s + 1 has landed; barrier; run stage s's
+  // MFMAs, issuing stage s + 3 into the slot of stage s - 1 (every wave
+  // finished it in iteration s - 1) between them (a burst of loads from all
+  // waves right after the barrier would fill the address queue and stall the
+  // waves' MFMA issue), and reading each half of stage s + 1's activations
+  // once the same half of stage s is consumed.
   // Issue order: chunk 0, stages 0..2; then per iteration s scale chunk
   // s/8 + 1 when s % 8 == 0 (its buffer held chunk s/8 - 1, whose last
   // reader, iteration s - 1, came before barrier s + 1), then stage s + 3.
@@ -257,12 +272,15 @@ __device__ __forceinline__ void run_item(uint8_t* lds, const Item& it, int K, in
   // a scale chunk went out in iteration i (before stage i + 3)
   auto chunk_at = [&](int i) { return scl_wave && i >= 0 && i % kScStages == 0 && i + kScStages < nst; };
   Acts ba, bb;
-  read_acts(0, ba);
+  read_acts(0, 0, ba);
+  read_acts(0, 1, ba);
   // one iteration; PREFETCH (a stage s + 1 exists) is false only for the
-  // last stage, so the loop body is straight-line code and the compiler's
-  // LDS counter waits stay exact
-  auto step = [&](auto prefetch, int s, Acts& cur, Acts& nxt) {
+  // last stage and ISSUE (a stage s + 3 exists) for the last three, so the
+  // loop body is straight-line code and the compiler's counter waits stay
+  // exact
+  auto step = [&](auto prefetch, auto issue_next, int s, Acts& cur, Acts& nxt) {
     constexpr bool PREFETCH = decltype(prefetch)::value;
+    constexpr bool ISSUE = decltype(issue_next)::value;
     uint2 cw[kASub];
     uint32_t sb[kASub];
     if constexpr (NV > 0) {
@@ -285,23 +303,41 @@ __device__ __forceinline__ void run_item(uint8_t* lds, const Item& it, int K, in
         __builtin_amdgcn_s_waitcnt(MXM_VMCNT(0));
       }
       wg_barrier();
-      if (s + kRing - 1 < nst) {
+      if constexpr (ISSUE) {
         if (chunk_at(s)) issue_scales(s / kScStages + 1);
-        issue(s + kRing - 1);
       }
-      read_acts(s + 1, nxt);
     }
-    compute(cw, sb, cur);
+    constexpr int kEvery = 2 * kASub / kLoadsPerStage;   // MFMA groups between loads
+    static_assert(kEvery * kLoadsPerStage == 2 * kASub, "loads spread evenly");
+    compute(cw, sb, cur, [&](int j) {
+      if constexpr (ISSUE) {
+        if (j % kEvery == 0) issue_one(s + kRing - 1, j / kEvery);
+      }
+    }, [&](int kk) {
+      if constexpr (PREFETCH) read_acts(s + 1, kk, nxt);
+    });
+    if constexpr (ISSUE && NV > 0) {
+      // ask the scheduler for: load, 2 NV MFMAs, load, 2 NV MFMAs, ...
+#pragma unroll
+      for (int q = 0; q < kLoadsPerStage; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);            // one VMEM read
+        __builtin_amdgcn_sched_group_barrier(0x008, kEvery * NV, 0);  // MFMAs
+      }
+    }
   };
   using yes = std::integral_constant<bool, true>;
   using no = std::integral_constant<bool, false>;
+  // nst is a multiple of 8: stages 0 .. nst - 5 in pairs, then nst - 4 (the
+  // last to issue), nst - 3, nst - 2 and nst - 1
   int s = 0;
-  for (; s + 2 < nst; s += 2) {
-    step(yes(), s, ba, bb);
-    step(yes(), s + 1, bb, ba);
+  for (; s + 4 < nst; s += 2) {
+    step(yes(), yes(), s, ba, bb);
+    step(yes(), yes(), s + 1, bb, ba);
   }
-  step(yes(), s, ba, bb);            // nst is even: stages nst - 2 and nst - 1
-  step(no(), s + 1, bb, ba);
+  step(yes(), yes(), s, ba, bb);
+  step(yes(), no(), s + 1, bb, ba);
+  step(yes(), no(), s + 2, ba, bb);
+  step(no(), no(), s + 3, bb, ba);
 
   // epilogue: lane holds D[4g+v][r16]: weight row 4g+v of subtile a, token
   // row r16 of subtile wm + kWM i

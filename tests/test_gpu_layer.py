@@ -37,6 +37,10 @@ DENSE = [
     ("dense_one_tile", (300, 512, 512, 8, 4), "uniform"),
     ("dense_two_tiles", (700, 512, 1024, 4, 2), "uniform"),
     ("dense_mixed_zipf", (256, 1024, 512, 64, 8), "zipf"),
+    # one expert: 192 + 8 rows, so the second m-tile leaves some waves without
+    # token rows; 192 + 20 rows, a partial subtile for every wave
+    ("dense_tail_8", (200, 512, 512, 1, 1), "uniform"),
+    ("dense_tail_20", (212, 1024, 512, 1, 1), "uniform"),
 ]
 
 # shapes that take the persistent decode kernel (H, I multiples of 2048, at
