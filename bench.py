@@ -43,14 +43,25 @@ ENTRY_KERNELS = {
     "moe_mxfp4_gate_up_swiglu": ("k_decode<true>", "k_gate_up<", "k_dense<true>"),
     "moe_mxfp4_down": ("k_decode<false>", "k_down<", "k_dense<false>"),
 }
-KERNEL_SOURCES = ("expert_decode.hip", "expert_stream.hip", "expert_dense.hip", "common.hpp")
+# source file of each kernel family; every measurement also depends on the
+# shared helpers and on the host code that picks the kernel
+KERNEL_FILES = {"k_decode": "expert_decode.hip", "k_gate_up": "expert_stream.hip",
+                "k_down": "expert_stream.hip", "k_dense": "expert_dense.hip"}
+COMMON_FILES = ("common.hpp", "expert_stream.hip", "api.hip")
 
 
-def kernel_source_hash():
+def kernel_sources(kernel_names):
+    files = set(COMMON_FILES)
+    for n in kernel_names:
+        files.update(f for k, f in KERNEL_FILES.items() if k in n)
+    return sorted(files)
+
+
+def kernel_source_hash(files):
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in files:
         with open(os.path.join(ROOT, "mxfp4_moe_expert_route_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+            h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
 
 
@@ -62,7 +73,8 @@ def measured_traffic(kernel, workload):
         return None
     with open(path) as f:
         rec = json.load(f).get("%s@%s" % (kernel, workload))
-    if not rec or rec.get("source_hash") != kernel_source_hash():
+    if not rec or "sources" not in rec or \
+            rec.get("source_hash") != kernel_source_hash(rec["sources"]):
         return None
     return rec.get("bytes_per_launch")
 
@@ -145,6 +157,7 @@ def summarize_profiles(args):
     if args.fetch_dir and args.write_dir:
         known = cfg.E * 2 * cfg.I * cfg.H // 2          # the w13 codes clone
         per = {}
+        names = {}
         factors = {}
         for ctr, d in (("FETCH_SIZE", args.fetch_dir), ("WRITE_SIZE", args.write_dir)):
             rows = [r for r in _csv_rows(_find_csv(d, "counter_collection.csv"))
@@ -158,6 +171,7 @@ def summarize_profiles(args):
                     if any(p in r["Kernel_Name"] for p in pats):
                         by_kernel.setdefault(r["Kernel_Name"], []).append(
                             float(r["Counter_Value"]))
+                names.setdefault(entry, set()).update(by_kernel)
                 per.setdefault(entry, {})[ctr] = sum(
                     np.mean(v) * 1024.0 * factors[ctr] for v in by_kernel.values())
         alg = _algorithmic_bytes(cfg, np.load(args.counts) if args.counts else
@@ -175,8 +189,10 @@ def summarize_profiles(args):
             out.append("| %s | %.1f | %.1f | %.1f | %.1f | %.3f |" % (
                 entry, v["FETCH_SIZE"] / 1e6, v["WRITE_SIZE"] / 1e6, tot / 1e6,
                 alg[entry] / 1e6, tot / alg[entry]))
+            srcs = kernel_sources(names[entry])
             db["%s@%s" % (entry, cfg.name)] = {
-                "source_hash": kernel_source_hash(), "bytes_per_launch": int(round(tot)),
+                "sources": srcs, "source_hash": kernel_source_hash(srcs),
+                "bytes_per_launch": int(round(tot)),
                 "fetch_bytes": int(round(v["FETCH_SIZE"])),
                 "write_bytes": int(round(v["WRITE_SIZE"])),
                 "algorithmic_bytes": int(alg[entry]),
@@ -322,6 +338,21 @@ def main():
         log("cpu baseline: %.3f tokens/s (%s)" % (cpu["value"], cpu["sample"]))
 
     traffic = measured_traffic("moe_mxfp4_gate_up_swiglu", cfg.name)
+    # the gate/up contraction is bound by HBM when its flops per algorithmic
+    # byte are below the machine balance (bf16 MFMA peak / HBM peak), else by
+    # the matrix cores
+    gu_flops = 4.0 * T * k * H * I
+    if gu_flops / gu_bytes < BF16_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9):
+        roofline = {"kernel": "moe_mxfp4_gate_up_swiglu", "bound": "hbm",
+                    "achieved": round(gu_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": round(gu_gbps / HBM_PEAK_GBPS, 4)}
+    else:
+        tflops = gu_flops / (gu_ms * 1e-3) / 1e12
+        roofline = {"kernel": "moe_mxfp4_gate_up_swiglu", "bound": "mfma",
+                    "achieved": round(tflops, 1), "peak": BF16_MFMA_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4)}
+    roofline.update({"traffic": traffic, "algorithmic_bytes": gu_bytes,
+                     "algorithmic_flops": gu_flops, "mean_launch_ms": round(gu_ms, 5)})
     line = {
         "metric": METRIC,
         "value": round(tokens_per_s, 1),
@@ -342,11 +373,7 @@ def main():
         "effective_weight_GBps": round(eff_gbps, 1),
         "hbm_frac_layer": round(eff_gbps / HBM_PEAK_GBPS, 4),
         "mfma_frac_layer": round(flops / (ms_step * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
-        "roofline": {"kernel": "moe_mxfp4_gate_up_swiglu", "bound": "hbm",
-                     "achieved": round(gu_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(gu_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic, "algorithmic_bytes": gu_bytes,
-                     "mean_launch_ms": round(gu_ms, 5)},
+        "roofline": roofline,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
