@@ -15,10 +15,12 @@
 // one m-tile read the same activation rows from that XCD's L2.  An m-tile
 // covers every row of a typical expert, so each weight byte leaves HBM once.
 //
-// The loads are sized by cache lines, the currency of the CU's load path: a
-// stage reads 32 code bytes of each weight row and 128 activation bytes (one
-// line) of each token row; the scale bytes of a row arrive 16 at a time (8
-// stages' worth) in a separate chunk buffer.
+// The loads are sized by cache lines, the currency of the CU's load path:
+// weight codes arrive 128 bytes (a whole line, four stages' worth) per row in
+// a super-stage, activations 64 bytes of each token row per load, and the
+// scale bytes of a row 16 at a time (8 stages' worth) in a separate chunk
+// buffer.  Weights are read once, so their loads carry the non-temporal hint
+// and leave the L2 to the activations, which every n-tile re-reads.
 //
 // Workgroup: 8 waves in a 4 x 2 grid, two per SIMD; wave (wn, wm) computes
 // 64 weight rows (4 subtiles of 16) x 96 token rows (the 16-row subtiles wm,
@@ -29,12 +31,14 @@
 // workgroup's 256 weight rows are 128 gate columns and the same 128 up
 // columns; wave wn holds 32 of each, so SwiGLU pairs inside the wave.
 //
-// A stage is 64 of K (two MX blocks).  Every wave issues its share of the
-// stage's asynchronous global->LDS loads (1 KB of codes, 3 x 1 KB of
-// activations, and every 8 stages, for waves 0-3, 1 KB of scales) into a
-// ring of four.  Operands are read from LDS one stage ahead: in the
-// iteration that runs stage s's MFMAs the wave reads stage s+1's operands,
-// so LDS latency hides behind MFMAs; one barrier per stage.
+// A stage is 64 of K (two MX blocks).  Activations go through a ring of
+// three stages: every wave issues its three 1 KB blocks of stage s + 3 while
+// it runs stage s's MFMAs, and reads stage s + 1's operands into registers
+// in the same iteration, so LDS latency hides behind MFMAs.  Weight codes go
+// through two super-stage slots of 32 KB: the four 1 KB loads per wave of
+// super-stage S + 2 are issued right after the barriers of iterations
+// 4S + 3 and 4S + 4, when every wave has read the last of super-stage S.
+// Waves 0-3 load 1 KB of scale bytes every 8 stages.  One barrier per stage.
 //
 // Register roles follow v_mfma_f32_16x16x32_bf16: weights are operand A
 // (row = weight row), activations operand B (row = token row).  In a stage,
@@ -46,9 +50,9 @@
 // read finds its 16 bytes (row r, K chunk 2g + kk) at 16 l, so every operand
 // read is one contiguous 1 KB; the load that fills a block fetches those 64
 // pieces (half of each of 16 rows' 128 bytes).  Row-strided layouts, even
-// xor-swizzled ones, read at about half that rate on gfx950.  Weight rows are
-// 32 bytes; row r keeps its two 16-byte blocks swapped when bit 3 of r is
-// set, which makes the 8-byte code reads conflict-free.
+// xor-swizzled ones, read at about half that rate on gfx950.  A weight
+// super-stage keeps each row's 128 bytes together, 16-byte block b in slot
+// b ^ ((row >> 1) & 7), which makes the 8-byte code reads conflict-free.
 #include <type_traits>
 
 #include "common.hpp"
@@ -59,29 +63,34 @@ namespace {
 constexpr int kMT = 192;             // token rows per tile
 constexpr int kNT = 256;             // weight rows per tile
 constexpr int kKS = 64;              // K per stage (2 MX blocks)
-constexpr int kRing = 4;             // stages in the LDS ring
+constexpr int kRingA = 3;            // activation stages in the LDS ring
+constexpr int kSS = 4;               // stages per weight super-stage (128 code bytes per row)
+constexpr int kRingW = 2;            // weight super-stage slots
 constexpr int kWaves = 8;
 constexpr int kDThreads = kWaves * kWave;
 constexpr int kMinRows = 64;         // experts with fewer rows use the streaming kernels
 constexpr int kMaxE = 1024;
-constexpr int kWB = kNT * kKS / 2;   // 8 KB of codes per stage
 constexpr int kAB = kMT * kKS * 2;   // 24 KB of activations per stage
-constexpr int kStage = kWB + kAB;
+constexpr int kWSlot = kNT * kKS * kSS / 2;   // 32 KB of codes per super-stage
 constexpr int kScStages = 8;         // stages per scale chunk (16 blocks = 16 B per row)
 constexpr int kSChunk = kNT * 16;    // 4 KB
-constexpr int kLdsS = kRing * kStage;
+constexpr int kLdsA = 0;
+constexpr int kLdsW = kLdsA + kRingA * kAB;
+constexpr int kLdsS = kLdsW + kRingW * kWSlot;
 constexpr int kLdsMpre = kLdsS + 2 * kSChunk;
 constexpr int kLdsBytes = kLdsMpre + (kMaxE + 4) * 4;
-constexpr int kActLoads = kAB / 1024 / kWaves;   // 3
-constexpr int kLoadsPerStage = 1 + kActLoads;     // per wave: 1 code and 3 activation loads
+constexpr int kActLoads = kAB / 1024 / kWaves;    // 3 per wave per stage
+constexpr int kWLoads = kWSlot / 1024 / kWaves;   // 4 per wave per super-stage
 constexpr int kWN = 4;                            // waves along weight rows
 constexpr int kWM = kWaves / kWN;                 // waves along token rows (2)
 constexpr int kASub = kNT / kWN / 16;             // weight subtiles per wave (4)
 constexpr int kMSub = kMT / 16 / kWM;             // token subtiles per wave (6)
+constexpr int kNT_AUX = 2;                        // buffer-load cache policy: non-temporal
 static_assert(kLdsBytes <= 160 * 1024, "LDS per CU");
-static_assert(kWB == kWaves * 1024 && kAB == kActLoads * kWaves * 1024 && kSChunk == 4 * 1024,
-              "every wave issues the same stage loads; waves 0-3 one scale load each");
-static_assert((kRing - 2) * kLoadsPerStage <= 63, "vmcnt range");
+static_assert(kAB == kActLoads * kWaves * 1024 && kWSlot == kWLoads * kWaves * 1024 &&
+              kSChunk == 4 * 1024 && kWLoads == 4,
+              "every wave issues the same loads; waves 0-3 one scale load each");
+static_assert(kScStages % kSS == 0 && kRingA == 3 && kRingW == 2, "the pipeline below");
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -93,17 +102,17 @@ __device__ __forceinline__ lds_void* lds_at(uint8_t* base, int off) {
   return (lds_void*)(base + off);   // generic -> LDS address space
 }
 
-// at most PER * n loads of this wave outstanding, n in [0, NMAX]
-template <int PER, int NMAX>
-__device__ __forceinline__ void vmcnt_wait_stages(int n) {
-  if constexpr (NMAX > 0) {
-    if (n >= NMAX) {
-      __builtin_amdgcn_s_waitcnt(MXM_VMCNT(PER * NMAX));
-      return;
-    }
-    vmcnt_wait_stages<PER, NMAX - 1>(n);
-  } else {
-    __builtin_amdgcn_s_waitcnt(MXM_VMCNT(0));
+// at most n (0..7) loads of this wave outstanding
+__device__ __forceinline__ void vmcnt_le(int n) {
+  switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(MXM_VMCNT(0)); break;
+    case 1: __builtin_amdgcn_s_waitcnt(MXM_VMCNT(1)); break;
+    case 2: __builtin_amdgcn_s_waitcnt(MXM_VMCNT(2)); break;
+    case 3: __builtin_amdgcn_s_waitcnt(MXM_VMCNT(3)); break;
+    case 4: __builtin_amdgcn_s_waitcnt(MXM_VMCNT(4)); break;
+    case 5: __builtin_amdgcn_s_waitcnt(MXM_VMCNT(5)); break;
+    case 6: __builtin_amdgcn_s_waitcnt(MXM_VMCNT(6)); break;
+    default: __builtin_amdgcn_s_waitcnt(MXM_VMCNT(7)); break;
   }
 }
 
@@ -152,7 +161,9 @@ __device__ __forceinline__ void run_item(uint8_t* lds, const Item& it, int K, in
   const int r16 = lane & 15, g = lane >> 4;
   const int wn = wave % kWN, wm = wave / kWN;
   const int nst = K / kKS;
+  const int nss = nst / kSS;
   const int nblk = K / 32;
+  const int rowb = K / 2;                 // code bytes per weight row
 
   // ---- this lane's load sources
   // activations: load j = wave + 8q fills the block of subtile j/2, MFMA
@@ -169,38 +180,36 @@ __device__ __forceinline__ void run_item(uint8_t* lds, const Item& it, int K, in
     voff[q] = src * uint32_t(K * 2) + uint32_t((2 * g + (j & 1)) * 16) +
               (uint32_t(tr >= it.rows) << 31);
   }
-  // codes: load i = wave covers local rows 32i..32i+31; lane -> row
-  // 32i + lane/2, slot parity lane&1 holding block (lane&1) ^ ((row>>3)&1)
-  const uint8_t* wsrc;
-  {
-    const int r = 32 * wave + (lane >> 1);
-    const int b = (lane & 1) ^ ((r >> 3) & 1);
-    wsrc = codes + weight_row<GU>(it.e, it.n, r, I, H) * (K / 2) + b * 16;
-  }
+  // codes: a buffer over this item's weight rows (gate/up: 128 gate rows,
+  // then from row I on the 128 up rows).  Load q of a super-stage covers
+  // local rows 64q + 8 wave .. 64q + 8 wave + 7; lane -> row 64q + rl, slot
+  // lane%8 holding 16-byte block (lane%8) ^ ((rl >> 1) & 7) of the row's 128
+  // super-stage bytes.
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(codes + weight_row<GU>(it.e, it.n, 0, I, H) * rowb), 0,
+      (GU ? I + 128 : kNT) * rowb, 0x00020000);
+  const int rl = 8 * wave + (lane >> 3);
+  const uint32_t wvoff = uint32_t(rl * rowb + 16 * ((lane & 7) ^ ((rl >> 1) & 7)));
+  auto issue_w = [&](int W, int q) {      // load q of super-stage W
+    const int r0 = GU ? (q >> 1) * I + 64 * (q & 1) : 64 * q;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rw, lds_at(lds, kLdsW + (W & 1) * kWSlot + 1024 * (wave + kWaves * q)), 16, wvoff,
+        r0 * rowb + 128 * W, 0, kNT_AUX);
+  };
   // scales (waves 0-3): local rows 64 wave + lane, 16 bytes (8 stages) each
   const bool scl_wave = wave < 4;
   const uint8_t* ssrc =
       scales + weight_row<GU>(it.e, it.n, 64 * (wave & 3) + lane, I, H) * nblk;
-
   auto issue_scales = [&](int c) {            // chunk c: stages 8c..8c+7
     if (scl_wave)
       __builtin_amdgcn_global_load_lds(ssrc + 16 * c,
                                        lds_at(lds, kLdsS + (c & 1) * kSChunk + 1024 * wave), 16,
                                        0, 0);
   };
-  // load q of stage s: q = 0 the codes, q = 1.. the activation blocks
-  auto issue_one = [&](int s, int q) {
-    uint8_t* st = lds + (s % kRing) * kStage;
-    if (q == 0)
-      __builtin_amdgcn_global_load_lds(wsrc + s * 32, lds_at(st, 1024 * wave), 16, 0, 0);
-    else
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, lds_at(st, kWB + 1024 * (wave + kWaves * (q - 1))), 16,
-          voff[q - 1] + uint32_t(s * kKS * 2), 0, 0, 0);
-  };
-  auto issue = [&](int s) {
-#pragma unroll
-    for (int q = 0; q < kLoadsPerStage; ++q) issue_one(s, q);
+  auto issue_a = [&](int s, int q) {      // activation load q of stage s
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, lds_at(lds, kLdsA + (s % kRingA) * kAB + 1024 * (wave + kWaves * q)), 16,
+        voff[q] + uint32_t(s * kKS * 2), 0, 0, 0);
   };
 
   f32x4 acc[kASub][NV > 0 ? NV : 1];
@@ -209,9 +218,9 @@ __device__ __forceinline__ void run_item(uint8_t* lds, const Item& it, int K, in
 #pragma unroll
     for (int i = 0; i < NV; ++i) acc[a][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // every subtile row's place in the stage: a base plus a constant per subtile
-  // (subtile rows are multiples of 16, so the swizzle bits come from r16)
-  const int wbase = 16 * (2 * r16 + ((g >> 1) ^ ((r16 >> 3) & 1))) + 8 * (g & 1);
+  // every subtile row's place: a base plus a constant per subtile (subtile
+  // rows are multiples of 16, so the swizzle bits come from r16)
+  const int sw = (r16 >> 1) & 7;
   const int sbase = 16 * r16 + (g >> 1);
   int abase[2];
 #pragma unroll
@@ -223,7 +232,7 @@ __device__ __forceinline__ void run_item(uint8_t* lds, const Item& it, int K, in
   typedef uint4 Acts[2][NV > 0 ? NV : 1];
   auto read_acts = [&](int s, int kk, Acts& b) {
     if constexpr (NV > 0) {
-      const uint8_t* st = lds + (s % kRing) * kStage + kWB;
+      const uint8_t* st = lds + kLdsA + (s % kRingA) * kAB;
 #pragma unroll
       for (int i = 0; i < NV; ++i)
         b[kk][i] = *reinterpret_cast<const uint4*>(st + abase[kk] + 2048 * kWM * i);
@@ -252,25 +261,44 @@ __device__ __forceinline__ void run_item(uint8_t* lds, const Item& it, int K, in
     }
   };
 
-  // Pipeline.  Iteration s: read stage s's codes and scale bytes (landed at
-  // barrier s); wait until stage s + 1 has landed; barrier; run stage s's
-  // MFMAs, issuing stage s + 3 into the slot of stage s - 1 (every wave
-  // finished it in iteration s - 1) between them (a burst of loads from all
-  // waves right after the barrier would fill the address queue and stall the
-  // waves' MFMA issue), and reading each half of stage s + 1's activations
-  // once the same half of stage s is consumed.
-  // Issue order: chunk 0, stages 0..2; then per iteration s scale chunk
-  // s/8 + 1 when s % 8 == 0 (its buffer held chunk s/8 - 1, whose last
-  // reader, iteration s - 1, came before barrier s + 1), then stage s + 3.
-  // nst is a multiple of 8.
-  static_assert(kRing == 4, "stages s - 1 .. s + 2 in the ring while s + 3 loads");
+  // Pipeline.  Iteration s: read stage s's codes and scale bytes; wait until
+  // stage s + 1 has landed; barrier; issue the scale chunk and weight loads
+  // due in this iteration; run stage s's MFMAs, issuing stage s + 3's
+  // activations into the slot of stage s (read in iteration s - 1) between
+  // them (a burst of loads from all waves right after the barrier would fill
+  // the address queue and stall the waves' MFMA issue), and reading each half
+  // of stage s + 1's activations once the same half of stage s is consumed.
+  // Weight super-stage W goes into slot W % 2 in iterations 4W - 5 (loads 0,
+  // 1) and 4W - 4 (loads 2, 3): the slot's previous super-stage W - 2 was
+  // last read at the top of iteration 4W - 5, before its barrier.  Scale
+  // chunk c goes out in iteration 8c - 8 (its buffer held chunk c - 2, last
+  // read at the top of iteration 8c - 9).  Everything a wave needs at
+  // barrier s + 1 (stage s + 1 and its codes and scales) was issued by
+  // iteration s - 1, so the wait at iteration s allows the loads of
+  // iteration s - 1 to be in flight.  nst is a multiple of 8, nss of 2.
+  auto chunk_at = [&](int i) { return scl_wave && i % kScStages == 0 && i + kScStages < nst; };
+  auto w_at = [&](int i) {                // super-stage whose loads go out in iteration i
+    const int t = i % kSS;
+    const int W = t == kSS - 1 ? i / kSS + 2 : (t == 0 && i >= kSS) ? i / kSS + 1 : nss;
+    return W < nss ? W : -1;
+  };
+  auto loads_in = [&](int i) {            // loads this wave issues in iteration i
+    return (i + kRingA < nst ? kActLoads : 0) + (w_at(i) >= 0 ? 2 : 0) + (chunk_at(i) ? 1 : 0);
+  };
+  // prologue: chunk 0, super-stage 0, stage 0, super-stage 1, stages 1, 2
   issue_scales(0);
 #pragma unroll
-  for (int p = 0; p < kRing - 1; ++p) issue(p);
-  __builtin_amdgcn_s_waitcnt(MXM_VMCNT(2 * kLoadsPerStage));    // chunk 0, stage 0
+  for (int q = 0; q < kWLoads; ++q) issue_w(0, q);
+#pragma unroll
+  for (int q = 0; q < kActLoads; ++q) issue_a(0, q);
+#pragma unroll
+  for (int q = 0; q < kWLoads; ++q) issue_w(1, q);
+#pragma unroll
+  for (int p = 1; p < kRingA; ++p)
+#pragma unroll
+    for (int q = 0; q < kActLoads; ++q) issue_a(p, q);
+  __builtin_amdgcn_s_waitcnt(MXM_VMCNT(kWLoads + 2 * kActLoads));   // chunk 0, W 0, stage 0
   wg_barrier();
-  // a scale chunk went out in iteration i (before stage i + 3)
-  auto chunk_at = [&](int i) { return scl_wave && i >= 0 && i % kScStages == 0 && i + kScStages < nst; };
   Acts ba, bb;
   read_acts(0, 0, ba);
   read_acts(0, 1, ba);
@@ -284,45 +312,46 @@ __device__ __forceinline__ void run_item(uint8_t* lds, const Item& it, int K, in
     uint2 cw[kASub];
     uint32_t sb[kASub];
     if constexpr (NV > 0) {
-      const uint8_t* st = lds + (s % kRing) * kStage;
+      const uint8_t* ws = lds + kLdsW + ((s / kSS) & 1) * kWSlot + 128 * r16 +
+                          16 * ((2 * (s % kSS) + (g >> 1)) ^ sw) + 8 * (g & 1);
       const uint8_t* sc = lds + kLdsS + ((s / kScStages) & 1) * kSChunk + 2 * (s % kScStages);
 #pragma unroll
       for (int a = 0; a < kASub; ++a) {
         const int lr = local_row<GU>(wn, a);
-        cw[a] = *reinterpret_cast<const uint2*>(st + wbase + 32 * lr);
+        cw[a] = *reinterpret_cast<const uint2*>(ws + 128 * lr);
         sb[a] = sc[sbase + 16 * lr];
       }
     }
     if constexpr (PREFETCH) {
-      // issued after stage s + 1 (in iteration s - 2): stage s + 2 and the
-      // chunk of iteration s - 1
-      if (s + 2 < nst) {
-        if (chunk_at(s - 1)) __builtin_amdgcn_s_waitcnt(MXM_VMCNT(kLoadsPerStage + 1));
-        else __builtin_amdgcn_s_waitcnt(MXM_VMCNT(kLoadsPerStage));
-      } else {
-        __builtin_amdgcn_s_waitcnt(MXM_VMCNT(0));
-      }
+      vmcnt_le(s == 0 ? kActLoads : loads_in(s - 1));
       wg_barrier();
-      if constexpr (ISSUE) {
-        if (chunk_at(s)) issue_scales(s / kScStages + 1);
+      if (chunk_at(s)) issue_scales(s / kScStages + 1);
+      const int W = w_at(s);
+      if (W >= 0) {
+        const int q0 = (s % kSS == kSS - 1) ? 0 : 2;
+        issue_w(W, q0);
+        issue_w(W, q0 + 1);
       }
     }
-    constexpr int kEvery = 2 * kASub / kLoadsPerStage;   // MFMA groups between loads
-    static_assert(kEvery * kLoadsPerStage == 2 * kASub, "loads spread evenly");
+    constexpr int kEvery = 3;               // MFMA groups between activation loads
+    static_assert(kEvery * (kActLoads - 1) < 2 * kASub, "loads inside the stage");
     compute(cw, sb, cur, [&](int j) {
       if constexpr (ISSUE) {
-        if (j % kEvery == 0) issue_one(s + kRing - 1, j / kEvery);
+        if (j % kEvery == 0 && j / kEvery < kActLoads) issue_a(s + kRingA, j / kEvery);
       }
     }, [&](int kk) {
       if constexpr (PREFETCH) read_acts(s + 1, kk, nxt);
     });
     if constexpr (ISSUE && NV > 0) {
-      // ask the scheduler for: load, 2 NV MFMAs, load, 2 NV MFMAs, ...
-#pragma unroll
-      for (int q = 0; q < kLoadsPerStage; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);            // one VMEM read
-        __builtin_amdgcn_sched_group_barrier(0x008, kEvery * NV, 0);  // MFMAs
-      }
+      // ask the scheduler for: load, 3 NV MFMAs, load, 3 NV MFMAs, load, 2 NV
+      // MFMAs (0x020: VMEM reads, 0x008: MFMAs)
+      static_assert(kActLoads == 3, "three loads per stage");
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, kEvery * NV, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, kEvery * NV, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, (2 * kASub - 2 * kEvery) * NV, 0);
     }
   };
   using yes = std::integral_constant<bool, true>;
@@ -469,12 +498,14 @@ hipError_t launch_dense(const uint16_t* act, uint32_t act_bytes, const int32_t* 
 
 // The dense path needs K to be whole scale chunks, the n-tiles whole (128
 // gate columns, 256 output rows), E within the LDS table and byte offsets of
-// activation rows that fit the 31-bit range of buffer addressing.
+// activation rows and of one item's weight rows that fit the 31-bit range
+// of buffer addressing.
 bool dense_supported(int T, int H, int I, int E, int k) {
   const int64_t R = int64_t(T) * k;
   if (H % 512 || I % 512 || E > kMaxE) return false;
   if (int64_t(T) * H * 2 + H * 2 >= (int64_t(1) << 31)) return false;
   if (R * I * 2 + I * 2 >= (int64_t(1) << 31)) return false;
+  if (int64_t(I + 128) * H / 2 >= (int64_t(1) << 31)) return false;   // one item's code rows
   return R >= kMinRows;
 }
 
