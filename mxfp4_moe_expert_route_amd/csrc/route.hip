@@ -9,8 +9,8 @@
 // Each logit becomes a 64-bit key: an order-preserving 32-bit image of the
 // float in the high word and (0xffffffff - index) in the low word, so the
 // unsigned maximum is the largest logit with the lowest index.  k rounds of a
-// wave-wide max (per-lane max, then a butterfly over ds_swizzle/DPP lanes)
-// pick the experts; the picked key is cleared to 0, below every valid key.
+// wave-wide max (per-lane max, then DPP row shifts and row broadcasts) pick
+// the experts; the picked key is cleared to 0, below every valid key.
 #include "common.hpp"
 
 namespace mxm {
@@ -29,6 +29,43 @@ __device__ __forceinline__ float key_value(uint32_t key) {
 
 __device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 
+// v moved across lanes by the DPP control CTRL (rows and banks masked by
+// RM); lanes whose source is outside the row read 0, below every key
+template <int CTRL, int RM>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, int(uint32_t(v)), CTRL, RM, 0xf, true);
+  const int hi = __builtin_amdgcn_update_dpp(0, int(uint32_t(v >> 32)), CTRL, RM, 0xf, true);
+  return (uint64_t(uint32_t(hi)) << 32) | uint32_t(lo);
+}
+
+// Largest key of the wave, in every lane.  Row shifts build each 16-lane
+// row's maximum in its lane 15, two row broadcasts carry them to lane 63;
+// DPP keeps the whole reduction in the VALU (no LDS round trips).
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  v = max_u64(v, dpp_u64<0x111, 0xf>(v));   // row_shr:1
+  v = max_u64(v, dpp_u64<0x112, 0xf>(v));   // row_shr:2
+  v = max_u64(v, dpp_u64<0x114, 0xf>(v));   // row_shr:4
+  v = max_u64(v, dpp_u64<0x118, 0xf>(v));   // row_shr:8
+  v = max_u64(v, dpp_u64<0x142, 0xa>(v));   // row_bcast:15 into rows 1 and 3
+  v = max_u64(v, dpp_u64<0x143, 0xc>(v));   // row_bcast:31 into rows 2 and 3
+  const uint32_t lo = __builtin_amdgcn_readlane(int(uint32_t(v)), kWave - 1);
+  const uint32_t hi = __builtin_amdgcn_readlane(int(uint32_t(v >> 32)), kWave - 1);
+  return (uint64_t(hi) << 32) | lo;
+}
+
+// Sum over the wave in a fixed order (the same reduction tree as above), in
+// every lane.
+__device__ __forceinline__ float wave_sum_f32(float v) {
+  auto add = [&](float x, int y) { return x + __int_as_float(y); };
+  v = add(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xf, 0xf, true));
+  v = add(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xf, 0xf, true));
+  v = add(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xf, 0xf, true));
+  v = add(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xf, 0xf, true));
+  v = add(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xa, 0xf, true));
+  v = add(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xc, 0xf, true));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), kWave - 1));
+}
+
 template <int NPER>
 __global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ logits, int T,
                                                     int E, int k, int32_t* __restrict__ ids,
@@ -45,29 +82,22 @@ __global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ lo
                      : 0ull;
   }
   int my_id = 0;
-  float my_l = 0.f;
+  float my_l = 0.f, l1 = 0.f;
   for (int j = 0; j < k; ++j) {
     uint64_t best = key[0];
 #pragma unroll
     for (int i = 1; i < NPER; ++i) best = max_u64(best, key[i]);
-#pragma unroll
-    for (int d = kWave / 2; d >= 1; d >>= 1) {
-      const uint32_t lo = __shfl_xor(uint32_t(best), d);
-      const uint32_t hi = __shfl_xor(uint32_t(best >> 32), d);
-      best = max_u64(best, (uint64_t(hi) << 32) | lo);
-    }
+    best = wave_max_u64(best);
 #pragma unroll
     for (int i = 0; i < NPER; ++i) key[i] = (key[i] == best) ? 0ull : key[i];
+    if (j == 0) l1 = key_value(uint32_t(best >> 32));
     if (lane == j) {
       my_id = int(0xffffffffu - uint32_t(best));
       my_l = key_value(uint32_t(best >> 32));
     }
   }
-  const float l1 = __shfl(my_l, 0);
-  float ex = (lane < k) ? expf(my_l - l1) : 0.f;
-  float sum = ex;
-#pragma unroll
-  for (int d = kWave / 2; d >= 1; d >>= 1) sum += __shfl_xor(sum, d);
+  const float ex = (lane < k) ? expf(my_l - l1) : 0.f;
+  const float sum = wave_sum_f32(ex);
   if (lane < k) {
     ids[int64_t(t) * k + lane] = my_id;
     w[int64_t(t) * k + lane] = ex / sum;
