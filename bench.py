@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MXFP4 MoE layer tokens/s + effective weight GB/s (% HBM peak) on 1 MI355X"
 HBM_PEAK_GBPS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
+FP32_VALU_PEAK_TFLOPS = 157.3
 
 
 def log(*a):
@@ -204,6 +205,54 @@ def summarize_profiles(args):
     print("\n".join(out))
 
 
+def bench_router(args, cfg, torch, mm, workloads):
+    """One JSON line for moe_router_topk on the workload's tokens: the fp32
+    router weights [E, H] are read once per block of tokens, so at decode
+    sizes the call streams them from HBM; above, fp32 FMAs bound it."""
+    dev = torch.device("cuda:0")
+    steps = args.steps or 200
+    warmup = args.warmup if args.warmup is not None else 20
+    T, H, E, k = cfg.T, cfg.H, cfg.E, cfg.k
+    x = torch.from_numpy(workloads.gen_x_bits(cfg, 0).view(np.int16)).view(torch.bfloat16).to(dev)
+    w = [torch.from_numpy(workloads.gen_router(cfg, 0)).to(dev) for _ in range(2)]
+    bias = torch.from_numpy(workloads.gen_bias(cfg, 0).astype(np.float32)).to(dev)
+    logits = torch.empty(T, E, dtype=torch.float32, device=dev)
+    ids = torch.empty(T, k, dtype=torch.int32, device=dev)
+    tw = torch.empty(T, k, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        mm.moe_router_topk(x, w[i & 1], k, bias, logits, ids, tw)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        mm.moe_router_topk(x, w[i & 1], k, bias, logits, ids, tw)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    nbytes = E * H * 4 + T * H * 2 + E * 4 + T * E * 4 + T * k * 8
+    flops = 2.0 * T * E * H
+    if flops / nbytes < FP32_VALU_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9):
+        ach = nbytes / (ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBPS, 4)}
+    else:
+        ach = flops / (ms * 1e-3) / 1e12
+        roof = {"bound": "alu", "achieved": round(ach, 2), "peak": FP32_VALU_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / FP32_VALU_PEAK_TFLOPS, 4)}
+    roof.update({"kernel": "moe_router_topk", "algorithmic_bytes": nbytes,
+                 "algorithmic_flops": flops, "mean_launch_ms": round(ms, 5), "traffic": None})
+    print(json.dumps({
+        "metric": "router projection + top-k tokens/s on 1 MI355X", "value": round(T / (ms * 1e-3), 1),
+        "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": cfg.name + " router", "tokens": T, "hidden": H, "experts": E,
+                   "top_k": k, "router_weights": "f32 [E, H]", "parallelism": "none (1 GPU)"},
+        "roofline": roof, "cpu_baseline": None}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -213,6 +262,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for cpu_baseline (0 disables)")
     ap.add_argument("--breakdown", action="store_true", help="per-kernel times on stderr")
+    ap.add_argument("--router", action="store_true",
+                    help="time moe_router_topk (router projection + top-k) instead of the layer")
     ap.add_argument("--save-counts", default=None,
                     help="write the per-expert row counts of the workload to this .npy")
     ap.add_argument("--summarize", action="store_true",
@@ -240,6 +291,9 @@ def main():
     import workloads
 
     cfg = workloads.CONFIGS[args.config]
+    if args.router:
+        bench_router(args, cfg, torch, mm, workloads)
+        return
     steps = args.steps or (200 if cfg.T <= 512 else 30)
     warmup = args.warmup if args.warmup is not None else (20 if cfg.T <= 512 else 5)
     dev = torch.device("cuda:0")

@@ -111,6 +111,29 @@ int mxfp4_unpack(const uint8_t* codes, const uint8_t* scales, int64_t rows,
 int moe_route_topk(const float* logits, int T, int E, int k,
                    int32_t* topk_ids, float* topk_w, void* stream);
 
+/*
+ * moe_router_topk — router projection, then moe_route_topk on its result.
+ *   x_bf16   [T, H] bf16, read; 8-byte aligned
+ *   w_router [E, H] f32, read (row e: expert e's router weights); 16-byte
+ *            aligned
+ *   bias     [E] f32 added to every token's logits, read; may be NULL
+ *   logits   [T, E] f32, written: x_t . w_e accumulated in fp32 (the products
+ *            of bf16 and fp32 values rounded by fused multiply-adds), plus
+ *            bias_e
+ *   topk_ids, topk_w: as moe_route_topk, computed from the written logits
+ * The pages route each token to 8 of 384 experts (nxbn.cn article,
+ * "架构设计与配置详解") with a hidden size of 6144 ("MiMo-V2.5-Pro-FP4-DFlash"
+ * model card, §4 "Model Summary") and give no router form; a linear
+ * projection of the bf16 hidden state with fp32 weights is the reading.
+ * H must be a multiple of 4 (up to 2^20).  Ids and weights are exactly what
+ * moe_route_topk gives for the written logits; the logits are deterministic
+ * run to run (fixed summation order) and lie within fp32 accumulation error
+ * of the exact sum.
+ */
+int moe_router_topk(const uint16_t* x_bf16, const float* w_router, const float* bias,
+                    int T, int H, int E, int k, float* logits, int32_t* topk_ids,
+                    float* topk_w, void* stream);
+
 /* Workspace moe_permute needs for these sizes (currently always 0). */
 size_t moe_permute_workspace_bytes(int T, int E, int k);
 

@@ -10,6 +10,7 @@ constexpr int kMaxE = 1024;
 constexpr int kMaxK = 32;
 constexpr int kMaxH = 16384;
 constexpr int kMaxI = 8192;
+constexpr int kMaxRouterH = 1 << 20;     // size_t row offsets; int loop bounds
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -94,6 +95,23 @@ int moe_route_topk(const float* logits, int T, int E, int k, int32_t* topk_ids, 
   if (!logits || !topk_ids || !topk_w) return MXM_ERR_NULL;
   if (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4)) return MXM_ERR_ALIGN;
   return launched(mxm::launch_route_topk(logits, T, E, k, topk_ids, topk_w, as_stream(stream)));
+}
+
+int moe_router_topk(const uint16_t* x_bf16, const float* w_router, const float* bias, int T,
+                    int H, int E, int k, float* logits, int32_t* topk_ids, float* topk_w,
+                    void* stream) {
+  const int st = check_route_shape(T, E, k);
+  if (st != MXM_OK) return st;
+  if (H < 4 || H % 4 || H > kMaxRouterH) return MXM_ERR_SHAPE;
+  if (T == 0) return MXM_OK;
+  if (!x_bf16 || !w_router || !logits || !topk_ids || !topk_w) return MXM_ERR_NULL;
+  if (!aligned(x_bf16, 8) || !aligned(w_router, 16) || !aligned(logits, 4) ||
+      !aligned(topk_ids, 4) || !aligned(topk_w, 4) || (bias && !aligned(bias, 4)))
+    return MXM_ERR_ALIGN;
+  const hipStream_t s = as_stream(stream);
+  if (mxm::launch_router_logits(x_bf16, w_router, bias, T, H, E, logits, s) != hipSuccess)
+    return MXM_ERR_LAUNCH;
+  return launched(mxm::launch_route_topk(logits, T, E, k, topk_ids, topk_w, s));
 }
 
 size_t moe_permute_workspace_bytes(int T, int E, int k) {

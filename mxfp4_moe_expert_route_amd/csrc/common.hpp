@@ -112,6 +112,8 @@ hipError_t launch_unpack(const uint8_t* codes, const uint8_t* scales, int64_t ro
                          void* y, int y_dtype, hipStream_t s);
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
                              hipStream_t s);
+hipError_t launch_router_logits(const uint16_t* x, const float* w_router, const float* bias, int T,
+                                int H, int E, float* logits, hipStream_t s);
 hipError_t launch_permute(const int32_t* ids, int T, int E, int k, int32_t* counts,
                           int32_t* offsets, int32_t* sorted_pairs, int32_t* pair_to_row,
                           hipStream_t s);

@@ -66,7 +66,10 @@ constexpr int kKS = 64;              // K per stage (2 MX blocks)
 constexpr int kRingA = 3;            // activation stages in the LDS ring
 constexpr int kSS = 4;               // stages per weight super-stage (128 code bytes per row)
 constexpr int kRingW = 2;            // weight super-stage slots
-constexpr int kWaves = 8;
+#ifndef MXM_DENSE_WAVES
+#define MXM_DENSE_WAVES 8
+#endif
+constexpr int kWaves = MXM_DENSE_WAVES;
 constexpr int kDThreads = kWaves * kWave;
 constexpr int kMinRows = 64;         // experts with fewer rows use the streaming kernels
 constexpr int kMaxE = 1024;
@@ -79,17 +82,18 @@ constexpr int kLdsW = kLdsA + kRingA * kAB;
 constexpr int kLdsS = kLdsW + kRingW * kWSlot;
 constexpr int kLdsMpre = kLdsS + 2 * kSChunk;
 constexpr int kLdsBytes = kLdsMpre + (kMaxE + 4) * 4;
-constexpr int kActLoads = kAB / 1024 / kWaves;    // 3 per wave per stage
-constexpr int kWLoads = kWSlot / 1024 / kWaves;   // 4 per wave per super-stage
+constexpr int kActLoads = kAB / 1024 / kWaves;    // per wave per stage
+constexpr int kWLoads = kWSlot / 1024 / kWaves;   // per wave per super-stage
 constexpr int kWN = 4;                            // waves along weight rows
-constexpr int kWM = kWaves / kWN;                 // waves along token rows (2)
+constexpr int kWM = kWaves / kWN;                 // waves along token rows
 constexpr int kASub = kNT / kWN / 16;             // weight subtiles per wave (4)
-constexpr int kMSub = kMT / 16 / kWM;             // token subtiles per wave (6)
+constexpr int kMSub = kMT / 16 / kWM;             // token subtiles per wave
 constexpr int kNT_AUX = 2;                        // buffer-load cache policy: non-temporal
 static_assert(kLdsBytes <= 160 * 1024, "LDS per CU");
 static_assert(kAB == kActLoads * kWaves * 1024 && kWSlot == kWLoads * kWaves * 1024 &&
-              kSChunk == 4 * 1024 && kWLoads == 4,
+              kSChunk == 4 * 1024 && kWLoads % 2 == 0 && kWaves >= 4,
               "every wave issues the same loads; waves 0-3 one scale load each");
+static_assert(kActLoads + kWLoads / 2 + 1 <= 15, "loads per iteration within vmcnt_le");
 static_assert(kScStages % kSS == 0 && kRingA == 3 && kRingW == 2, "the pipeline below");
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -102,7 +106,7 @@ __device__ __forceinline__ lds_void* lds_at(uint8_t* base, int off) {
   return (lds_void*)(base + off);   // generic -> LDS address space
 }
 
-// at most n (0..7) loads of this wave outstanding
+// at most n (0..15) loads of this wave outstanding
 __device__ __forceinline__ void vmcnt_le(int n) {
   switch (n) {
     case 0: __builtin_amdgcn_s_waitcnt(MXM_VMCNT(0)); break;
@@ -112,7 +116,15 @@ __device__ __forceinline__ void vmcnt_le(int n) {
     case 4: __builtin_amdgcn_s_waitcnt(MXM_VMCNT(4)); break;
     case 5: __builtin_amdgcn_s_waitcnt(MXM_VMCNT(5)); break;
     case 6: __builtin_amdgcn_s_waitcnt(MXM_VMCNT(6)); break;
-    default: __builtin_amdgcn_s_waitcnt(MXM_VMCNT(7)); break;
+    case 7: __builtin_amdgcn_s_waitcnt(MXM_VMCNT(7)); break;
+    case 8: __builtin_amdgcn_s_waitcnt(MXM_VMCNT(8)); break;
+    case 9: __builtin_amdgcn_s_waitcnt(MXM_VMCNT(9)); break;
+    case 10: __builtin_amdgcn_s_waitcnt(MXM_VMCNT(10)); break;
+    case 11: __builtin_amdgcn_s_waitcnt(MXM_VMCNT(11)); break;
+    case 12: __builtin_amdgcn_s_waitcnt(MXM_VMCNT(12)); break;
+    case 13: __builtin_amdgcn_s_waitcnt(MXM_VMCNT(13)); break;
+    case 14: __builtin_amdgcn_s_waitcnt(MXM_VMCNT(14)); break;
+    default: __builtin_amdgcn_s_waitcnt(MXM_VMCNT(15)); break;
   }
 }
 
@@ -142,6 +154,19 @@ template <bool GU>
 __device__ __forceinline__ int64_t weight_row(int e, int n, int r, int I, int H) {
   if constexpr (GU) return int64_t(e) * 2 * I + (r < 128 ? 0 : I) + 128 * n + (r & 127);
   else return int64_t(e) * H + kNT * n + r;
+}
+
+// Scheduling pattern for one stage: N times (one VMEM read, then M MFMAs),
+// the last group LAST MFMAs (0x020: VMEM reads, 0x008: MFMAs).
+template <int N, int M, int LAST>
+__device__ __forceinline__ void sched_loads_between_mfma() {
+  __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+  if constexpr (N == 1) {
+    __builtin_amdgcn_sched_group_barrier(0x008, LAST, 0);
+  } else {
+    __builtin_amdgcn_sched_group_barrier(0x008, M, 0);
+    sched_loads_between_mfma<N - 1, M, LAST>();
+  }
 }
 
 struct Item {
@@ -182,7 +207,7 @@ __device__ __forceinline__ void run_item(uint8_t* lds, const Item& it, int K, in
   }
   // codes: a buffer over this item's weight rows (gate/up: 128 gate rows,
   // then from row I on the 128 up rows).  Load q of a super-stage covers
-  // local rows 64q + 8 wave .. 64q + 8 wave + 7; lane -> row 64q + rl, slot
+  // local rows 8 (wave + W q) .. + 7 (W waves); lane -> row 8 W q + rl, slot
   // lane%8 holding 16-byte block (lane%8) ^ ((rl >> 1) & 7) of the row's 128
   // super-stage bytes.
   const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
@@ -191,7 +216,8 @@ __device__ __forceinline__ void run_item(uint8_t* lds, const Item& it, int K, in
   const int rl = 8 * wave + (lane >> 3);
   const uint32_t wvoff = uint32_t(rl * rowb + 16 * ((lane & 7) ^ ((rl >> 1) & 7)));
   auto issue_w = [&](int W, int q) {      // load q of super-stage W
-    const int r0 = GU ? (q >> 1) * I + 64 * (q & 1) : 64 * q;
+    const int lr0 = 8 * kWaves * q;        // first local row of the load (a multiple of 32)
+    const int r0 = GU && lr0 >= 128 ? I + lr0 - 128 : lr0;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         rw, lds_at(lds, kLdsW + (W & 1) * kWSlot + 1024 * (wave + kWaves * q)), 16, wvoff,
         r0 * rowb + 128 * W, 0, kNT_AUX);
@@ -283,7 +309,8 @@ __device__ __forceinline__ void run_item(uint8_t* lds, const Item& it, int K, in
     return W < nss ? W : -1;
   };
   auto loads_in = [&](int i) {            // loads this wave issues in iteration i
-    return (i + kRingA < nst ? kActLoads : 0) + (w_at(i) >= 0 ? 2 : 0) + (chunk_at(i) ? 1 : 0);
+    return (i + kRingA < nst ? kActLoads : 0) + (w_at(i) >= 0 ? kWLoads / 2 : 0) +
+           (chunk_at(i) ? 1 : 0);
   };
   // prologue: chunk 0, super-stage 0, stage 0, super-stage 1, stages 1, 2
   issue_scales(0);
@@ -328,12 +355,12 @@ __device__ __forceinline__ void run_item(uint8_t* lds, const Item& it, int K, in
       if (chunk_at(s)) issue_scales(s / kScStages + 1);
       const int W = w_at(s);
       if (W >= 0) {
-        const int q0 = (s % kSS == kSS - 1) ? 0 : 2;
-        issue_w(W, q0);
-        issue_w(W, q0 + 1);
+        const int q0 = (s % kSS == kSS - 1) ? 0 : kWLoads / 2;
+#pragma unroll
+        for (int q = 0; q < kWLoads / 2; ++q) issue_w(W, q0 + q);
       }
     }
-    constexpr int kEvery = 3;               // MFMA groups between activation loads
+    constexpr int kEvery = 2 * kASub / kActLoads > 0 ? 2 * kASub / kActLoads : 1;
     static_assert(kEvery * (kActLoads - 1) < 2 * kASub, "loads inside the stage");
     compute(cw, sb, cur, [&](int j) {
       if constexpr (ISSUE) {
@@ -343,15 +370,9 @@ __device__ __forceinline__ void run_item(uint8_t* lds, const Item& it, int K, in
       if constexpr (PREFETCH) read_acts(s + 1, kk, nxt);
     });
     if constexpr (ISSUE && NV > 0) {
-      // ask the scheduler for: load, 3 NV MFMAs, load, 3 NV MFMAs, load, 2 NV
-      // MFMAs (0x020: VMEM reads, 0x008: MFMAs)
-      static_assert(kActLoads == 3, "three loads per stage");
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, kEvery * NV, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, kEvery * NV, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, (2 * kASub - 2 * kEvery) * NV, 0);
+      // ask the scheduler for: load, kEvery NV MFMAs, load, ..., load, the
+      // rest of the MFMAs
+      sched_loads_between_mfma<kActLoads, kEvery * NV, (2 * kASub - kEvery * (kActLoads - 1)) * NV>();
     }
   };
   using yes = std::integral_constant<bool, true>;
@@ -398,6 +419,21 @@ __device__ __forceinline__ void run_item(uint8_t* lds, const Item& it, int K, in
         *reinterpret_cast<float4*>(y + row * H + col) = make_float4(v[0], v[1], v[2], v[3]);
       }
     }
+  }
+}
+
+// run_item with this wave's token subtile count as a constant
+template <bool GU, int N>
+__device__ __forceinline__ void run_nv(int nv, uint8_t* lds, const Item& it, int K, int I, int H,
+                                       int k, const __amdgpu_buffer_rsrc_t& rs,
+                                       const int32_t* __restrict__ sorted_pairs,
+                                       const uint8_t* __restrict__ codes,
+                                       const uint8_t* __restrict__ scales, void* __restrict__ out) {
+  if constexpr (N == 0) {
+    run_item<GU, 0>(lds, it, K, I, H, k, rs, sorted_pairs, codes, scales, out);
+  } else {
+    if (nv == N) run_item<GU, N>(lds, it, K, I, H, k, rs, sorted_pairs, codes, scales, out);
+    else run_nv<GU, N - 1>(nv, lds, it, K, I, H, k, rs, sorted_pairs, codes, scales, out);
   }
 }
 
@@ -451,15 +487,7 @@ __global__ __launch_bounds__(kDThreads, 1) void k_dense(
     const int nsub = (it.rows + 15) >> 4;
     const int nv =
         __builtin_amdgcn_readfirstlane(max(0, min(kMSub, (nsub - wm + kWM - 1) / kWM)));
-    switch (nv) {
-      case 6: run_item<GU, 6>(lds, it, K, I, H, k, rs, sorted_pairs, codes, scales, out); break;
-      case 5: run_item<GU, 5>(lds, it, K, I, H, k, rs, sorted_pairs, codes, scales, out); break;
-      case 4: run_item<GU, 4>(lds, it, K, I, H, k, rs, sorted_pairs, codes, scales, out); break;
-      case 3: run_item<GU, 3>(lds, it, K, I, H, k, rs, sorted_pairs, codes, scales, out); break;
-      case 2: run_item<GU, 2>(lds, it, K, I, H, k, rs, sorted_pairs, codes, scales, out); break;
-      case 1: run_item<GU, 1>(lds, it, K, I, H, k, rs, sorted_pairs, codes, scales, out); break;
-      default: run_item<GU, 0>(lds, it, K, I, H, k, rs, sorted_pairs, codes, scales, out); break;
-    }
+    run_nv<GU, kMSub>(nv, lds, it, K, I, H, k, rs, sorted_pairs, codes, scales, out);
     __syncthreads();                 // the ring is free for the next item
   }
 }

@@ -1,4 +1,5 @@
-// Top-k routing: one wave64 per token.
+// Top-k routing (one wave64 per token) and the router projection in front of
+// it.
 //
 // The pages give 384 experts with 8 active per token (nxbn.cn article,
 // "架构设计与配置详解") and no scoring rule.  Rule used (a reading): experts by
@@ -113,7 +114,174 @@ hipError_t launch_n(const float* logits, int T, int E, int k, int32_t* ids, floa
   return hipGetLastError();
 }
 
+// Router projection: logits[t][e] = sum_h x[t][h] * w[e][h] (+ bias[e]), fp32
+// accumulation in a fixed order (deterministic run to run).
+//
+// Decode sizes (T <= 64): one workgroup per expert and block of 8 tokens.
+// Its 256 lanes split the expert's weight row (float4 each, 1 KB strides), so
+// every load of the row is in flight at once and the row is read once per
+// token block; each lane keeps one fma chain per token, then a DPP tree per wave and the
+// four waves' sums in order.
+template <int TB>
+__global__ __launch_bounds__(256) void k_router_rows(const uint16_t* __restrict__ x,
+                                                     const float* __restrict__ wr,
+                                                     const float* __restrict__ bias, int T, int H,
+                                                     int E, float* __restrict__ logits) {
+  __shared__ float part[4][TB];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = lane_id();
+  const int e = blockIdx.x;
+  const int t0 = blockIdx.y * TB;
+  const int nt = min(TB, T - t0);
+  const float* wrow = wr + size_t(e) * H;
+  float acc[TB];
+#pragma unroll
+  for (int j = 0; j < TB; ++j) acc[j] = 0.f;
+#pragma unroll 6
+  for (int h = 4 * tid; h < H; h += 1024) {
+    const float4 w = *reinterpret_cast<const float4*>(wrow + h);
+#pragma unroll
+    for (int j = 0; j < TB; ++j) {
+      if (j < nt) {
+        const uint2 xv = *reinterpret_cast<const uint2*>(x + size_t(t0 + j) * H + h);
+        acc[j] = fmaf(__uint_as_float(xv.x << 16), w.x, acc[j]);
+        acc[j] = fmaf(__uint_as_float(xv.x & 0xffff0000u), w.y, acc[j]);
+        acc[j] = fmaf(__uint_as_float(xv.y << 16), w.z, acc[j]);
+        acc[j] = fmaf(__uint_as_float(xv.y & 0xffff0000u), w.w, acc[j]);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < TB; ++j) {
+    if (j < nt) {
+      const float sum = wave_sum_f32(acc[j]);
+      if (lane == 0) part[wave][j] = sum;
+    }
+  }
+  __syncthreads();
+  if (tid < nt) {
+    const float b = bias ? bias[e] : 0.f;
+    logits[size_t(t0 + tid) * E + e] = ((part[0][tid] + part[1][tid]) + (part[2][tid] + part[3][tid])) + b;
+  }
+}
+
+// Larger T: tiles of RT tokens x RE experts (64 x 64, or 32 x 32 when that
+// leaves too few workgroups), K in steps of 32 staged through LDS as fp32,
+// K-major.  Each lane computes RT/16 tokens x RE/16 experts: per K element a
+// vector of x and one of w from LDS feed all of its fmas.  The next step's
+// global loads are issued before the current step's fmas.  Each step's 32
+// products go into a fresh partial that is then added to the running total,
+// so an output sees 32-term chains and one add per step (H % 32 == 0).
+constexpr int kRK = 32;
+
+template <int RT, int RE>
+__global__ __launch_bounds__(256) void k_router_tiles(const uint16_t* __restrict__ x,
+                                                      const float* __restrict__ wr,
+                                                      const float* __restrict__ bias, int T,
+                                                      int H, int E, float* __restrict__ logits) {
+  constexpr int PT = RT / 16, PE = RE / 16;      // outputs per lane
+  constexpr int XL = RT * kRK / 256;             // x elements each lane stages (8 or 4)
+  constexpr int WL = RE * kRK / 256;             // w elements each lane stages
+  static_assert(XL == 8 || XL == 4, "x staged as 16 or 8 bytes per lane");
+  static_assert(WL == 8 || WL == 4, "w staged as 32 or 16 bytes per lane");
+  __shared__ __attribute__((aligned(16))) float xs[kRK][RT];
+  __shared__ __attribute__((aligned(16))) float ws[kRK][RE];
+  const int tid = threadIdx.x;
+  const int tx = tid & 15, ty = tid >> 4;        // experts PE tx.., tokens PT ty..
+  const int t0 = blockIdx.y * RT, e0 = blockIdx.x * RE;
+  // staging roles: x row tid / (32 / XL), K elements XL (tid % (32 / XL)) ..
+  const int xr = tid / (kRK / XL), xk = XL * (tid % (kRK / XL));
+  const int wrr = tid / (kRK / WL), wk = WL * (tid % (kRK / WL));
+  const uint16_t* xsrc = x + size_t(min(t0 + xr, T - 1)) * H + xk;
+  const float* wsrc = wr + size_t(min(e0 + wrr, E - 1)) * H + wk;
+  uint32_t xv[XL / 2];
+  float wv[WL];
+  auto fetch = [&](int k0) {
+    if constexpr (XL == 8) {
+      const uint4 v = *reinterpret_cast<const uint4*>(xsrc + k0);
+      xv[0] = v.x; xv[1] = v.y; xv[2] = v.z; xv[3] = v.w;
+    } else {
+      const uint2 v = *reinterpret_cast<const uint2*>(xsrc + k0);
+      xv[0] = v.x; xv[1] = v.y;
+    }
+#pragma unroll
+    for (int i = 0; i < WL; i += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(wsrc + k0 + i);
+      wv[i] = v.x; wv[i + 1] = v.y; wv[i + 2] = v.z; wv[i + 3] = v.w;
+    }
+  };
+  float tot[PT][PE];
+#pragma unroll
+  for (int i = 0; i < PT; ++i)
+#pragma unroll
+    for (int j = 0; j < PE; ++j) tot[i][j] = 0.f;
+  fetch(0);
+  for (int k0 = 0; k0 < H; k0 += kRK) {
+    __syncthreads();                             // the previous step's reads are done
+#pragma unroll
+    for (int i = 0; i < XL / 2; ++i) {
+      xs[xk + 2 * i][xr] = __uint_as_float(xv[i] << 16);
+      xs[xk + 2 * i + 1][xr] = __uint_as_float(xv[i] & 0xffff0000u);
+    }
+#pragma unroll
+    for (int i = 0; i < WL; ++i) ws[wk + i][wrr] = wv[i];
+    __syncthreads();
+    if (k0 + kRK < H) fetch(k0 + kRK);
+    float stp[PT][PE];
+#pragma unroll
+    for (int i = 0; i < PT; ++i)
+#pragma unroll
+      for (int j = 0; j < PE; ++j) stp[i][j] = 0.f;
+#pragma unroll 8
+    for (int kk = 0; kk < kRK; ++kk) {
+      float av[PT], bv[PE];
+#pragma unroll
+      for (int i = 0; i < PT; ++i) av[i] = xs[kk][PT * ty + i];
+#pragma unroll
+      for (int j = 0; j < PE; ++j) bv[j] = ws[kk][PE * tx + j];
+#pragma unroll
+      for (int i = 0; i < PT; ++i)
+#pragma unroll
+        for (int j = 0; j < PE; ++j) stp[i][j] = fmaf(av[i], bv[j], stp[i][j]);
+    }
+#pragma unroll
+    for (int i = 0; i < PT; ++i)
+#pragma unroll
+      for (int j = 0; j < PE; ++j) tot[i][j] += stp[i][j];
+  }
+#pragma unroll
+  for (int j = 0; j < PE; ++j) {
+    const int e = e0 + PE * tx + j;
+    if (e >= E) continue;
+    const float b = bias ? bias[e] : 0.f;
+#pragma unroll
+    for (int i = 0; i < PT; ++i) {
+      const int t = t0 + PT * ty + i;
+      if (t < T) logits[size_t(t) * E + e] = tot[i][j] + b;
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_router_logits(const uint16_t* x, const float* w_router, const float* bias, int T,
+                                int H, int E, float* logits, hipStream_t s) {
+  // the tiles load up to 16 bytes of x per lane: rows and base 16-byte aligned
+  if (T <= 64 || H % kRK || reinterpret_cast<uintptr_t>(x) % 16) {
+    // blocks of 8 tokens: more workgroups in flight beat fewer passes over the
+    // weights here (32-token blocks: 44 us against 32 us at 64 tokens)
+    const dim3 grid(unsigned(E), unsigned((T + 7) / 8));
+    k_router_rows<8><<<grid, 256, 0, s>>>(x, w_router, bias, T, H, E, logits);
+  } else if (int64_t((E + 63) / 64) * ((T + 63) / 64) >= 512) {
+    const dim3 grid(unsigned((E + 63) / 64), unsigned((T + 63) / 64));
+    k_router_tiles<64, 64><<<grid, 256, 0, s>>>(x, w_router, bias, T, H, E, logits);
+  } else {
+    const dim3 grid(unsigned((E + 31) / 32), unsigned((T + 31) / 32));
+    k_router_tiles<32, 32><<<grid, 256, 0, s>>>(x, w_router, bias, T, H, E, logits);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
                              hipStream_t s) {

@@ -81,6 +81,28 @@ def moe_route_topk(logits, k, topk_ids=None, topk_w=None):
     return topk_ids, topk_w
 
 
+def moe_router_topk(x, w_router, k, bias=None, logits=None, topk_ids=None, topk_w=None):
+    """x [T, H] bfloat16, w_router [E, H] float32 (bias [E] float32 or None)
+    -> (logits float32 [T, E], ids int32 [T, k], weights float32 [T, k])."""
+    _need(x, "x", torch.bfloat16)
+    _need(w_router, "w_router", torch.float32)
+    T, H = x.shape
+    E, H2 = w_router.shape
+    if H2 != H:
+        raise ValueError("w_router must be [E, H] with H = x.shape[1]")
+    if bias is not None:
+        _need(bias, "bias", torch.float32)
+        if tuple(bias.shape) != (E,):
+            raise ValueError("bias must be [E]")
+    logits = _out(logits, "logits", torch.float32, (T, E), x.device)
+    topk_ids = _out(topk_ids, "topk_ids", torch.int32, (T, k), x.device)
+    topk_w = _out(topk_w, "topk_w", torch.float32, (T, k), x.device)
+    check(lib().moe_router_topk(_ptr(x), _ptr(w_router), _ptr(bias) if bias is not None else None,
+                                T, H, E, k, _ptr(logits), _ptr(topk_ids), _ptr(topk_w),
+                                _stream()), "moe_router_topk")
+    return logits, topk_ids, topk_w
+
+
 def moe_permute_workspace_bytes(T, E, k):
     return int(lib().moe_permute_workspace_bytes(T, E, k))
 

@@ -18,15 +18,45 @@ here, listed in DESIGN.md, is:
 
 Inputs with a +inf logit, or with every logit -inf/NaN, have no defined
 weights and are outside the contract.
+
+`router_logits` is the projection in front of the routing (a further step,
+not part of the layer's own inputs): the pages give no router form, and the
+reading is a linear map of the bf16 hidden state with fp32 weights (plus an
+optional per-expert bias), summed exactly in float64 and rounded once to
+fp32.
 """
 
 import numpy as np
+
+from .mx import bf16_bits_to_f64
 
 
 def _clean(logits):
     l = np.asarray(logits, dtype=np.float64).copy()
     l[np.isnan(l)] = -np.inf
     return l
+
+
+def router_logits(x_bits, w_router, bias=None):
+    """x_bits uint16[T, H] (bf16), w_router float32[E, H], bias float32[E] or
+    None -> float32[T, E] = fp32(x . w_e (+ bias_e)).
+
+    Every product of a bf16 and an fp32 value is exact in float64 (8 + 24
+    significant bits), so the only rounding before the final one is float64
+    summation, far below fp32's."""
+    x = bf16_bits_to_f64(np.asarray(x_bits, dtype=np.uint16))
+    w = np.asarray(w_router, dtype=np.float32).astype(np.float64)
+    out = x @ w.T
+    if bias is not None:
+        out = out + np.asarray(bias, dtype=np.float32).astype(np.float64)[None, :]
+    return out.astype(np.float32)
+
+
+def router_abs_bound(x_bits, w_router):
+    """float64[T, E]: sum_h |x_th w_eh|, the scale of fp32 accumulation error."""
+    x = np.abs(bf16_bits_to_f64(np.asarray(x_bits, dtype=np.uint16)))
+    w = np.abs(np.asarray(w_router, dtype=np.float32).astype(np.float64))
+    return x @ w.T
 
 
 def expert_order(logits):

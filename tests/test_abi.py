@@ -29,7 +29,7 @@ def lib():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("mxfp4_pack", "mxfp4_unpack", "moe_route_topk", "moe_permute",
+    for n in ("mxfp4_pack", "mxfp4_unpack", "moe_route_topk", "moe_router_topk", "moe_permute",
               "moe_permute_workspace_bytes", "moe_mxfp4_gate_up_swiglu", "moe_mxfp4_down",
               "moe_combine", "moe_mxfp4_layer", "mxm_status_string", "mxm_version"):
         assert n in names
@@ -75,6 +75,20 @@ def test_route_permute_argument_checks(lib):
     assert lib.moe_permute_workspace_bytes(64, 384, 8) == 0
     assert lib.moe_permute(P, 4, 8, 2, P, P, P, None, None, 0, None) == -1
     assert lib.moe_permute(P, 4, 8, 9, P, P, P, P, None, 0, None) == -2
+
+
+def test_router_argument_checks(lib):
+    # x, w_router, bias, T, H, E, k, logits, ids, w, stream
+    assert lib.moe_router_topk(P, P, None, 4, 64, 8, 9, P, P, P, None) == -2     # k > E
+    assert lib.moe_router_topk(P, P, None, 4, 66, 8, 2, P, P, P, None) == -2     # H % 4
+    assert lib.moe_router_topk(P, P, None, 4, 0, 8, 2, P, P, P, None) == -2      # H = 0
+    assert lib.moe_router_topk(P, P, None, 4, 64, 1025, 8, P, P, P, None) == -2  # E > 1024
+    assert lib.moe_router_topk(None, P, None, 4, 64, 8, 2, P, P, P, None) == -1  # null x
+    assert lib.moe_router_topk(P, P, None, 4, 64, 8, 2, None, P, P, None) == -1  # null logits
+    assert lib.moe_router_topk(P + 4, P, None, 4, 64, 8, 2, P, P, P, None) == -4  # x 8-byte
+    assert lib.moe_router_topk(P, P + 8, None, 4, 64, 8, 2, P, P, P, None) == -4  # w 16-byte
+    assert lib.moe_router_topk(P, P, P + 2, 4, 64, 8, 2, P, P, P, None) == -4     # bias
+    assert lib.moe_router_topk(None, None, None, 0, 64, 8, 2, None, None, None, None) == 0
 
 
 def test_ffn_combine_argument_checks(lib):

@@ -115,3 +115,63 @@ def test_permute_matches_stable_argsort_construction(T, E, k, seed):
 def test_permute_rejects_out_of_range():
     with pytest.raises(ValueError):
         operm.permute(np.array([[0, 5]]), 4)
+
+
+# ---- router projection (the step in front of the routing)
+
+def _bf16_bits(v):
+    """float32 values that are exactly bf16 -> their bit patterns."""
+    b = np.asarray(v, np.float32).view(np.uint32)
+    assert np.all(b & 0xffff == 0)
+    return (b >> 16).astype(np.uint16)
+
+
+def test_router_logits_basis_vectors_pick_weight_columns():
+    rng = np.random.default_rng(11)
+    E, H = 6, 10
+    w = rng.standard_normal((E, H)).astype(np.float32)
+    x = np.eye(H, dtype=np.float32)                   # token i = unit vector i (1.0 is bf16)
+    l = oroute.router_logits(_bf16_bits(x), w)
+    assert l.shape == (H, E) and l.dtype == np.float32
+    assert np.array_equal(l, w.T)                     # exactly column i of w for token i
+    b = rng.standard_normal(E).astype(np.float32)
+    lb = oroute.router_logits(_bf16_bits(x), w, b)
+    assert np.array_equal(lb, (w.T.astype(np.float64) + b).astype(np.float32))
+
+
+def test_router_logits_exact_small_integer_case():
+    rng = np.random.default_rng(12)
+    T, E, H = 7, 5, 64
+    x = rng.integers(-2, 3, size=(T, H)).astype(np.float32)
+    wq = rng.integers(-4, 5, size=(E, H))
+    w = (wq / 8.0).astype(np.float32)                 # multiples of 1/8: every sum exact
+    want = (x.astype(np.int64) @ wq.T.astype(np.int64)) / 8.0
+    l = oroute.router_logits(_bf16_bits(x), w)
+    assert np.array_equal(l.astype(np.float64), want)
+
+
+def test_router_logits_brute_force_rational():
+    from fractions import Fraction
+    rng = np.random.default_rng(13)
+    T, E, H = 3, 4, 9
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    x = (x.view(np.uint32) & 0xffff0000).view(np.float32)     # truncate to bf16 values
+    w = rng.standard_normal((E, H)).astype(np.float32)
+    b = rng.standard_normal(E).astype(np.float32)
+    l = oroute.router_logits(_bf16_bits(x), w, b)
+    for t in range(T):
+        for e in range(E):
+            exact = sum(Fraction(float(x[t, h])) * Fraction(float(w[e, h])) for h in range(H))
+            exact += Fraction(float(b[e]))
+            got = Fraction(float(l[t, e]))
+            ulp = np.spacing(np.float32(abs(float(exact)))).astype(np.float64)
+            assert abs(got - exact) <= Fraction(float(ulp)) / 2 * Fraction(1001, 1000)
+
+
+def test_router_abs_bound_dominates_logits():
+    rng = np.random.default_rng(14)
+    x = rng.standard_normal((5, 32)).astype(np.float32)
+    x = (x.view(np.uint32) & 0xffff0000).view(np.float32)
+    w = rng.standard_normal((3, 32)).astype(np.float32)
+    xb = _bf16_bits(x)
+    assert np.all(np.abs(oroute.router_logits(xb, w)) <= oroute.router_abs_bound(xb, w) * (1 + 1e-6))
