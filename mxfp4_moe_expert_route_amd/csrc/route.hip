@@ -117,52 +117,69 @@ hipError_t launch_n(const float* logits, int T, int E, int k, int32_t* ids, floa
 // Router projection: logits[t][e] = sum_h x[t][h] * w[e][h] (+ bias[e]), fp32
 // accumulation in a fixed order (deterministic run to run).
 //
-// Decode sizes (T <= 64): one workgroup per expert and block of 8 tokens.
-// Its 256 lanes split the expert's weight row (float4 each, 1 KB strides), so
-// every load of the row is in flight at once and the row is read once per
-// token block; each lane keeps one fma chain per token, then a DPP tree per wave and the
-// four waves' sums in order.
-template <int TB>
+// Decode sizes (T <= 64): one workgroup per EPW experts and block of 8
+// tokens.  Its 256 lanes split the experts' weight rows (float4 each, 1 KB
+// strides), so every load of a row is in flight at once and each row is read
+// once per token block; each lane keeps one fma chain per (expert, token),
+// then a DPP tree per wave and the four waves' sums in order.
+template <int TB, int EPW>
 __global__ __launch_bounds__(256) void k_router_rows(const uint16_t* __restrict__ x,
                                                      const float* __restrict__ wr,
                                                      const float* __restrict__ bias, int T, int H,
                                                      int E, float* __restrict__ logits) {
-  __shared__ float part[4][TB];
+  __shared__ float part[4][EPW][TB];
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = lane_id();
-  const int e = blockIdx.x;
+  const int e0 = blockIdx.x * EPW;
+  const int ne = min(EPW, E - e0);
   const int t0 = blockIdx.y * TB;
   const int nt = min(TB, T - t0);
-  const float* wrow = wr + size_t(e) * H;
-  float acc[TB];
+  float acc[EPW][TB];
 #pragma unroll
-  for (int j = 0; j < TB; ++j) acc[j] = 0.f;
+  for (int q = 0; q < EPW; ++q)
+#pragma unroll
+    for (int j = 0; j < TB; ++j) acc[q][j] = 0.f;
 #pragma unroll 6
   for (int h = 4 * tid; h < H; h += 1024) {
-    const float4 w = *reinterpret_cast<const float4*>(wrow + h);
+    float4 w[EPW];
+#pragma unroll
+    for (int q = 0; q < EPW; ++q)
+      w[q] = *reinterpret_cast<const float4*>(wr + size_t(e0 + min(q, ne - 1)) * H + h);
 #pragma unroll
     for (int j = 0; j < TB; ++j) {
       if (j < nt) {
         const uint2 xv = *reinterpret_cast<const uint2*>(x + size_t(t0 + j) * H + h);
-        acc[j] = fmaf(__uint_as_float(xv.x << 16), w.x, acc[j]);
-        acc[j] = fmaf(__uint_as_float(xv.x & 0xffff0000u), w.y, acc[j]);
-        acc[j] = fmaf(__uint_as_float(xv.y << 16), w.z, acc[j]);
-        acc[j] = fmaf(__uint_as_float(xv.y & 0xffff0000u), w.w, acc[j]);
+        const float x0 = __uint_as_float(xv.x << 16), x1 = __uint_as_float(xv.x & 0xffff0000u);
+        const float x2 = __uint_as_float(xv.y << 16), x3 = __uint_as_float(xv.y & 0xffff0000u);
+#pragma unroll
+        for (int q = 0; q < EPW; ++q) {
+          acc[q][j] = fmaf(x0, w[q].x, acc[q][j]);
+          acc[q][j] = fmaf(x1, w[q].y, acc[q][j]);
+          acc[q][j] = fmaf(x2, w[q].z, acc[q][j]);
+          acc[q][j] = fmaf(x3, w[q].w, acc[q][j]);
+        }
       }
     }
   }
 #pragma unroll
-  for (int j = 0; j < TB; ++j) {
-    if (j < nt) {
-      const float sum = wave_sum_f32(acc[j]);
-      if (lane == 0) part[wave][j] = sum;
+  for (int q = 0; q < EPW; ++q)
+#pragma unroll
+    for (int j = 0; j < TB; ++j) {
+      if (j < nt) {
+        const float sum = wave_sum_f32(acc[q][j]);
+        if (lane == 0) part[wave][q][j] = sum;
+      }
     }
-  }
   __syncthreads();
-  if (tid < nt) {
-    const float b = bias ? bias[e] : 0.f;
-    logits[size_t(t0 + tid) * E + e] = ((part[0][tid] + part[1][tid]) + (part[2][tid] + part[3][tid])) + b;
+  if (tid < EPW * TB) {
+    const int q = tid / TB, j = tid % TB;
+    if (q < ne && j < nt) {
+      const int e = e0 + q;
+      const float b = bias ? bias[e] : 0.f;
+      logits[size_t(t0 + j) * E + e] =
+          ((part[0][q][j] + part[1][q][j]) + (part[2][q][j] + part[3][q][j])) + b;
+    }
   }
 }
 
@@ -269,10 +286,16 @@ hipError_t launch_router_logits(const uint16_t* x, const float* w_router, const 
                                 int H, int E, float* logits, hipStream_t s) {
   // the tiles load up to 16 bytes of x per lane: rows and base 16-byte aligned
   if (T <= 64 || H % kRK || reinterpret_cast<uintptr_t>(x) % 16) {
-    // blocks of 8 tokens: more workgroups in flight beat fewer passes over the
-    // weights here (32-token blocks: 44 us against 32 us at 64 tokens)
-    const dim3 grid(unsigned(E), unsigned((T + 7) / 8));
-    k_router_rows<8><<<grid, 256, 0, s>>>(x, w_router, bias, T, H, E, logits);
+    // blocks of 8 tokens (32-token blocks: 44 us against 31 us at 64 tokens);
+    // one expert per workgroup for a single block (15 us at 8 tokens, two:
+    // 15.5, four: 18.4), four when several blocks re-read the weights (21 us
+    // at 64 tokens against 31)
+    if (T <= 8) {
+      k_router_rows<8, 1><<<dim3(unsigned(E), 1), 256, 0, s>>>(x, w_router, bias, T, H, E, logits);
+    } else {
+      const dim3 grid(unsigned((E + 3) / 4), unsigned((T + 7) / 8));
+      k_router_rows<8, 4><<<grid, 256, 0, s>>>(x, w_router, bias, T, H, E, logits);
+    }
   } else if (int64_t((E + 63) / 64) * ((T + 63) / 64) >= 512) {
     const dim3 grid(unsigned((E + 63) / 64), unsigned((T + 63) / 64));
     k_router_tiles<64, 64><<<grid, 256, 0, s>>>(x, w_router, bias, T, H, E, logits);
