@@ -253,6 +253,51 @@ def bench_router(args, cfg, torch, mm, workloads):
         "roofline": roof, "cpu_baseline": None}), flush=True)
 
 
+def bench_verify(args, cfg, torch, mm, workloads):
+    """One JSON line for dflash_verify_accept: T / 8 drafted blocks of 8 over
+    the vocabulary; every input byte is read once (the draw re-reads one part
+    of one row per block), so the step streams from HBM."""
+    dev = torch.device("cuda:0")
+    steps = args.steps or 200
+    warmup = args.warmup if args.warmup is not None else 20
+    L, V = 8, workloads.VERIFY_VOCAB
+    B = max(1, cfg.T // L)
+    if B > 64:
+        print("bench.py: --verify runs workloads of up to 512 tokens (64 blocks)", file=sys.stderr)
+        sys.exit(2)
+    tg, dr, tk, u = workloads.gen_verify_inputs(B, L, V, 0)
+    ins = [tuple(torch.from_numpy(a).to(dev) for a in (tg, dr, tk, u)) for _ in range(2)]
+    n = torch.empty(B, dtype=torch.int32, device=dev)
+    t = torch.empty(B, dtype=torch.int32, device=dev)
+    ws = torch.empty(max(8, int(mm._lib.lib().dflash_verify_workspace_bytes(B, L, V))),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        mm.dflash_verify_accept(*ins[i & 1], n, t, ws)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        mm.dflash_verify_accept(*ins[i & 1], n, t, ws)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    nbytes = B * (2 * L + 1) * V * 4 + B * (2 * L + 1) * 4 + B * 8
+    ach = nbytes / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "drafted blocks verified per second on 1 MI355X", "value": round(B / (ms * 1e-3), 1),
+        "unit": "blocks/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": cfg.name + " verify", "blocks": B, "block": L, "vocab": V,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"kernel": "dflash_verify_accept", "bound": "hbm", "achieved": round(ach, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
+                     "algorithmic_bytes": nbytes, "mean_launch_ms": round(ms, 5), "traffic": None},
+        "cpu_baseline": None}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -264,6 +309,8 @@ def main():
     ap.add_argument("--breakdown", action="store_true", help="per-kernel times on stderr")
     ap.add_argument("--router", action="store_true",
                     help="time moe_router_topk (router projection + top-k) instead of the layer")
+    ap.add_argument("--verify", action="store_true",
+                    help="time dflash_verify_accept on the workload's sequences (T / 8 blocks of 8)")
     ap.add_argument("--save-counts", default=None,
                     help="write the per-expert row counts of the workload to this .npy")
     ap.add_argument("--summarize", action="store_true",
@@ -293,6 +340,9 @@ def main():
     cfg = workloads.CONFIGS[args.config]
     if args.router:
         bench_router(args, cfg, torch, mm, workloads)
+        return
+    if args.verify:
+        bench_verify(args, cfg, torch, mm, workloads)
         return
     steps = args.steps or (200 if cfg.T <= 512 else 30)
     warmup = args.warmup if args.warmup is not None else (20 if cfg.T <= 512 else 5)

@@ -134,6 +134,40 @@ int moe_router_topk(const uint16_t* x_bf16, const float* w_router, const float* 
                     int T, int H, int E, int k, float* logits, int32_t* topk_ids,
                     float* topk_w, void* stream);
 
+/* Workspace dflash_verify_accept needs (0 for invalid sizes). */
+size_t dflash_verify_workspace_bytes(int B, int L, int V);
+
+/*
+ * dflash_verify_accept — rejection-sampling verification of B drafted blocks
+ * of L tokens over a vocabulary of V.
+ *   target_logits [B, L+1, V] f32, read: the backbone's logits at the L block
+ *                 positions and the one after; 16-byte aligned
+ *   draft_probs   [B, L, V] f32, read: the drafter's probabilities; 16-byte
+ *                 aligned
+ *   draft_tokens  [B, L] int32, read: the drafted tokens
+ *   uniforms      [B, L+1] f32 in [0, 1), read: one per position, the last
+ *                 for the draw
+ *   accept_len    [B] int32, written: n, the leading positions accepted
+ *   next_token    [B] int32, written: the token after the n accepted ones
+ *   workspace     dflash_verify_workspace_bytes(B, L, V) bytes, 8-byte aligned
+ * The pages verify a whole drafted block in one backbone step with
+ * rejection sampling keeping the output lossless, blocks capped at 8
+ * ("MiMo-V2.5-Pro-FP4-DFlash" model card, §3 "Block-Diffusion Speculative
+ * Decoding (DFlash)").  The rule is the reading: with p_i = softmax of the
+ * logits (temperature 1) and q_i the drafter's probabilities, position i is
+ * accepted when u_i * q_i(d_i) < p_i(d_i); n counts the leading accepted
+ * positions; the next token is drawn with u_L from max(0, p_n - q_n) when
+ * n < L (from p_n if that is all zero) and from p_L when n = L, by inverse
+ * CDF in vocabulary order.  A drafted token outside [0, V) is rejected.
+ * 1 <= L <= 32, V a multiple of 4; a row with no finite logit is outside
+ * the contract.  Computed in fp32 in fixed orders (deterministic); decisions
+ * within fp32 rounding of a threshold may differ from exact arithmetic.
+ */
+int dflash_verify_accept(const float* target_logits, const float* draft_probs,
+                         const int32_t* draft_tokens, const float* uniforms, int B, int L,
+                         int V, int32_t* accept_len, int32_t* next_token, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
 /* Workspace moe_permute needs for these sizes (currently always 0). */
 size_t moe_permute_workspace_bytes(int T, int E, int k);
 

@@ -19,6 +19,9 @@ SIGNATURES = {
     "mxfp4_unpack": (_c_int, [_p, _p, _c_i64, _c_i64, _p, _c_int, _p]),
     "moe_route_topk": (_c_int, [_p, _c_int, _c_int, _c_int, _p, _p, _p]),
     "moe_router_topk": (_c_int, [_p, _p, _p, _c_int, _c_int, _c_int, _c_int, _p, _p, _p, _p]),
+    "dflash_verify_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int]),
+    "dflash_verify_accept": (_c_int, [_p, _p, _p, _p, _c_int, _c_int, _c_int, _p, _p, _p, _c_size,
+                                      _p]),
     "moe_permute_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int]),
     "moe_permute": (_c_int, [_p, _c_int, _c_int, _c_int, _p, _p, _p, _p, _p, _c_size, _p]),
     "moe_mxfp4_gate_up_swiglu": (_c_int, [_p, _p, _p, _c_int, _c_int, _c_int, _c_int, _c_int,

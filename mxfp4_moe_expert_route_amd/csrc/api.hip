@@ -11,6 +11,7 @@ constexpr int kMaxK = 32;
 constexpr int kMaxH = 16384;
 constexpr int kMaxI = 8192;
 constexpr int kMaxRouterH = 1 << 20;     // size_t row offsets; int loop bounds
+constexpr int kMaxVerifyL = 32;          // one lane of a wave per block position
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -112,6 +113,32 @@ int moe_router_topk(const uint16_t* x_bf16, const float* w_router, const float* 
   if (mxm::launch_router_logits(x_bf16, w_router, bias, T, H, E, logits, s) != hipSuccess)
     return MXM_ERR_LAUNCH;
   return launched(mxm::launch_route_topk(logits, T, E, k, topk_ids, topk_w, s));
+}
+
+size_t dflash_verify_workspace_bytes(int B, int L, int V) {
+  (void)V;
+  if (B < 0 || L < 1 || L > kMaxVerifyL) return 0;
+  return mxm::verify_workspace_bytes(B, L);
+}
+
+int dflash_verify_accept(const float* target_logits, const float* draft_probs,
+                         const int32_t* draft_tokens, const float* uniforms, int B, int L, int V,
+                         int32_t* accept_len, int32_t* next_token, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  if (B < 0 || L < 1 || L > kMaxVerifyL || V < 4 || V % 4) return MXM_ERR_SHAPE;
+  if (int64_t(B) * (L + 1) * V > (int64_t(1) << 40) || int64_t(B) * (L + 1) * 8 > INT32_MAX)
+    return MXM_ERR_SHAPE;
+  if (B == 0) return MXM_OK;
+  if (workspace_bytes < dflash_verify_workspace_bytes(B, L, V)) return MXM_ERR_WORKSPACE;
+  if (!target_logits || !draft_probs || !draft_tokens || !uniforms || !accept_len ||
+      !next_token || !workspace)
+    return MXM_ERR_NULL;
+  if (!aligned(target_logits, 16) || !aligned(draft_probs, 16) || !aligned(draft_tokens, 4) ||
+      !aligned(uniforms, 4) || !aligned(accept_len, 4) || !aligned(next_token, 4) ||
+      !aligned(workspace, 8))
+    return MXM_ERR_ALIGN;
+  return launched(mxm::launch_verify(target_logits, draft_probs, draft_tokens, uniforms, B, L, V,
+                                     accept_len, next_token, workspace, as_stream(stream)));
 }
 
 size_t moe_permute_workspace_bytes(int T, int E, int k) {

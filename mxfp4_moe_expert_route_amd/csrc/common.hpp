@@ -147,6 +147,11 @@ hipError_t launch_gate_up_dense(const uint16_t* x, const int32_t* sorted_pairs,
 hipError_t launch_down_dense(const uint16_t* h, const int32_t* offsets, int T, int H, int I,
                              int E, int k, const uint8_t* codes, const uint8_t* scales, float* y,
                              hipStream_t s);
+// Rejection-sampling verification of drafted blocks.
+size_t verify_workspace_bytes(int B, int L);
+hipError_t launch_verify(const float* target, const float* draft, const int32_t* tokens,
+                         const float* uniforms, int B, int L, int V, int32_t* accept_len,
+                         int32_t* next_token, void* workspace, hipStream_t s);
 hipError_t launch_combine(const float* y, const float* w, const int32_t* pair_to_row, int T,
                           int H, int k, float* out, hipStream_t s);
 

@@ -103,6 +103,33 @@ def moe_router_topk(x, w_router, k, bias=None, logits=None, topk_ids=None, topk_
     return logits, topk_ids, topk_w
 
 
+def dflash_verify_accept(target_logits, draft_probs, draft_tokens, uniforms, accept_len=None,
+                         next_token=None, workspace=None):
+    """target_logits [B, L+1, V] f32, draft_probs [B, L, V] f32, draft_tokens
+    [B, L] int32, uniforms [B, L+1] f32 -> (accept_len int32 [B], next_token
+    int32 [B])."""
+    _need(target_logits, "target_logits", torch.float32)
+    _need(draft_probs, "draft_probs", torch.float32)
+    _need(draft_tokens, "draft_tokens", torch.int32)
+    _need(uniforms, "uniforms", torch.float32)
+    B, L1, V = target_logits.shape
+    L = L1 - 1
+    if tuple(draft_probs.shape) != (B, L, V) or tuple(draft_tokens.shape) != (B, L) or \
+            tuple(uniforms.shape) != (B, L + 1):
+        raise ValueError("shapes must be [B, L+1, V], [B, L, V], [B, L], [B, L+1]")
+    dev = target_logits.device
+    accept_len = _out(accept_len, "accept_len", torch.int32, (B,), dev)
+    next_token = _out(next_token, "next_token", torch.int32, (B,), dev)
+    nbytes = int(lib().dflash_verify_workspace_bytes(B, L, V))
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 8), dtype=torch.uint8, device=dev)
+    check(lib().dflash_verify_accept(_ptr(target_logits), _ptr(draft_probs), _ptr(draft_tokens),
+                                     _ptr(uniforms), B, L, V, _ptr(accept_len), _ptr(next_token),
+                                     _ptr(workspace), workspace.numel(), _stream()),
+          "dflash_verify_accept")
+    return accept_len, next_token
+
+
 def moe_permute_workspace_bytes(T, E, k):
     return int(lib().moe_permute_workspace_bytes(T, E, k))
 

@@ -17,7 +17,8 @@ losslessness requirement it exists to meet:
     (from p_n itself in the degenerate case where r is all zero), and from
     p_L (the backbone's distribution after the block) when n = L;
   * a draw from weights w uses one uniform u: the smallest token v whose
-    running sum of w exceeds u * sum(w) (inverse CDF in vocabulary order).
+    running sum of w exceeds u * sum(w) (inverse CDF in vocabulary order);
+  * a drafted token outside the vocabulary is rejected.
 
 Every probability is computed in float64.  Random numbers are inputs.
 """
@@ -48,6 +49,9 @@ def verify_block(target_logits, draft_probs, draft_tokens, u):
     for i in range(L):
         p = softmax64(target_logits[i])
         d = int(draft_tokens[i])
+        if not 0 <= d < len(p):             # a token outside the vocabulary is rejected
+            n = i
+            break
         if not (float(u[i]) * float(draft_probs[i][d]) < p[d]):
             n = i
             break

@@ -29,7 +29,8 @@ def lib():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("mxfp4_pack", "mxfp4_unpack", "moe_route_topk", "moe_router_topk", "moe_permute",
+    for n in ("mxfp4_pack", "mxfp4_unpack", "moe_route_topk", "moe_router_topk",
+              "dflash_verify_accept", "dflash_verify_workspace_bytes", "moe_permute",
               "moe_permute_workspace_bytes", "moe_mxfp4_gate_up_swiglu", "moe_mxfp4_down",
               "moe_combine", "moe_mxfp4_layer", "mxm_status_string", "mxm_version"):
         assert n in names
@@ -89,6 +90,19 @@ def test_router_argument_checks(lib):
     assert lib.moe_router_topk(P, P + 8, None, 4, 64, 8, 2, P, P, P, None) == -4  # w 16-byte
     assert lib.moe_router_topk(P, P, P + 2, 4, 64, 8, 2, P, P, P, None) == -4     # bias
     assert lib.moe_router_topk(None, None, None, 0, 64, 8, 2, None, None, None, None) == 0
+
+
+def test_verify_argument_checks(lib):
+    ws = lib.dflash_verify_workspace_bytes(4, 8, 64)
+    assert ws > 0 and lib.dflash_verify_workspace_bytes(4, 33, 64) == 0
+    # target, draft, tokens, uniforms, B, L, V, accept_len, next_token, ws, bytes, stream
+    assert lib.dflash_verify_accept(P, P, P, P, 4, 8, 50, P, P, P, ws, None) == -2      # V % 4
+    assert lib.dflash_verify_accept(P, P, P, P, 4, 0, 64, P, P, P, ws, None) == -2      # L < 1
+    assert lib.dflash_verify_accept(P, P, P, P, 4, 33, 64, P, P, P, ws, None) == -2     # L > 32
+    assert lib.dflash_verify_accept(P, P, P, P, 4, 8, 64, P, P, P, ws - 1, None) == -7  # workspace
+    assert lib.dflash_verify_accept(None, P, P, P, 4, 8, 64, P, P, P, ws, None) == -1
+    assert lib.dflash_verify_accept(P + 4, P, P, P, 4, 8, 64, P, P, P, ws, None) == -4  # 16-byte
+    assert lib.dflash_verify_accept(None, None, None, None, 0, 8, 64, None, None, None, 0, None) == 0
 
 
 def test_ffn_combine_argument_checks(lib):

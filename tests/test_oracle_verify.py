@@ -100,3 +100,11 @@ def test_one_hot_backbone_accepts_exactly_its_token():
     assert n == 2 and t == 4        # position 2 drafted 5, the backbone only allows 4
     n, t = ov.verify_block(tl, q, [3, 1, 4], [0.9, 0.9, 0.9, 0.4])
     assert n == 3 and t == 2        # all accepted, bonus from position 3
+
+
+def test_token_outside_vocabulary_is_rejected():
+    V = 4
+    tl = np.zeros((3, V), np.float32)
+    q = np.full((2, V), 0.25, np.float32)
+    assert ov.verify_block(tl, q, [V, 0], [0.0, 0.0, 0.5])[0] == 0
+    assert ov.verify_block(tl, q, [1, -1], [0.0, 0.0, 0.5])[0] == 1

@@ -202,3 +202,28 @@ def layer_inputs(cfg, seed=0, weights=True):
     if weights:
         d.update(all_weights(cfg, seed))
     return d
+
+
+# ---- drafted blocks for the verification step (a "next" row) -------------
+
+VERIFY_VOCAB = 152064      # reading: the pages give only a mask token id of 151669
+
+
+def gen_verify_inputs(B, L=8, V=VERIFY_VOCAB, seed=0, logit_std=3.0, draft_noise=0.35):
+    """Synthetic inputs of B drafted blocks: backbone logits [B, L+1, V] ~
+    N(0, logit_std^2); drafter probabilities [B, L, V] = softmax of the
+    backbone logits plus N(0, draft_noise^2) (per-token acceptance about
+    0.88, about 4.6 of 8 tokens accepted on average); drafted tokens drawn from
+    the drafter's probabilities; uniforms in [0, 1).  All float32 / int32."""
+    r = _rng(seed, 77, B, L, V)
+    target = r.normal(0.0, logit_std, size=(B, L + 1, V)).astype(np.float32)
+    noisy = target[:, :L, :].astype(np.float64) + r.normal(0.0, draft_noise, size=(B, L, V))
+    noisy -= noisy.max(axis=2, keepdims=True)
+    q = np.exp(noisy)
+    q /= q.sum(axis=2, keepdims=True)
+    draft = q.astype(np.float32)
+    c = np.cumsum(q, axis=2)
+    pick = r.random((B, L, 1)) * c[:, :, -1:]
+    tokens = np.minimum((c <= pick).sum(axis=2), V - 1).astype(np.int32)
+    uniforms = np.minimum(r.random((B, L + 1)), 1.0 - 2.0 ** -24).astype(np.float32)
+    return target, draft, tokens, uniforms
