@@ -255,8 +255,11 @@ def bench_router(args, cfg, torch, mm, workloads):
 
 def bench_verify(args, cfg, torch, mm, workloads):
     """One JSON line for dflash_verify_accept: T / 8 drafted blocks of 8 over
-    the vocabulary; every input byte is read once (the draw re-reads one part
-    of one row per block), so the step streams from HBM."""
+    the vocabulary.  Algorithmic bytes per block: the L + 1 rows of target
+    logits, the drafter's row at the first rejected position, the drafter's
+    probabilities at the L drafted tokens, the tokens, the uniforms and the
+    two outputs.  The kernels read target row n a second time (from cache
+    when it is still there); that re-read is not counted."""
     dev = torch.device("cuda:0")
     steps = args.steps or 200
     warmup = args.warmup if args.warmup is not None else 20
@@ -283,7 +286,7 @@ def bench_verify(args, cfg, torch, mm, workloads):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
-    nbytes = B * (2 * L + 1) * V * 4 + B * (2 * L + 1) * 4 + B * 8
+    nbytes = B * ((L + 2) * V * 4 + L * 4 + L * 4 + (L + 1) * 4 + 8)
     ach = nbytes / (ms * 1e-3) / 1e9
     print(json.dumps({
         "metric": "drafted blocks verified per second on 1 MI355X", "value": round(B / (ms * 1e-3), 1),
