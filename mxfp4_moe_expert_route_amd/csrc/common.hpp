@@ -49,14 +49,17 @@ __device__ __forceinline__ bf16x8 dequant8(uint32_t codes, float scale) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-// Inclusive prefix sum across the 64 lanes of a wave (all lanes active).
+// Inclusive prefix sum across the 64 lanes of a wave (all lanes active), in
+// DPP steps: shifts by 1, 2, 4, 8 within each row of 16 lanes, then lane 15
+// of rows 0 and 2 added into rows 1 and 3, then lane 31 into rows 2 and 3.
+// Lanes whose source is out of range add 0.
 __device__ __forceinline__ int wave_incl_scan(int v) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    int o = __shfl_up(v, d);
-    if (lane >= d) v += o;
-  }
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, true);   // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, true);   // row_bcast:31
   return v;
 }
 

@@ -70,12 +70,11 @@ constexpr int kLdsActs = kRing * kStageB;                       // 16 rows x 1 K
 constexpr int kLdsScales = kLdsActs + kTokRows * 1024;          // 256 rows x K/32
 constexpr int kLdsUnits = kLdsScales + kUnitRows * (kMaxK / 32);
 constexpr int kLdsDec = kLdsUnits + kMaxUnits * 16;
-// set-up tables live in the activation buffer until the first chunk lands
-constexpr int kLdsOffs = kLdsActs;                              // offsets[0..E]
-constexpr int kLdsTpre = kLdsActs + (kMaxE + 4) * 4;            // tiles before expert e
+// the set-up's per-wave sums live in the activation buffer until the first chunk lands
+constexpr int kLdsWsum = kLdsActs;
 static_assert(kPerLoader * kCW * 1024 == kStageB, "whole loads per stage");
 static_assert((kRing - 2) * kPerLoader <= 63, "vmcnt counts at most 63 loads");
-static_assert(kLdsTpre + (kMaxE + 4) * 4 <= kLdsScales, "set-up tables fit the act buffer");
+static_assert(2 * kThreadsDec >= kMaxE, "two experts per thread in the set-up");
 static_assert(kLdsDec <= 160 * 1024, "LDS per CU");
 
 __device__ __forceinline__ lds_void* lds_at(uint8_t* base, int off) {
@@ -111,18 +110,6 @@ __device__ __forceinline__ int4v lds_read_i32x4(const uint8_t* p) {
   int4v v;
   asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_addr(p)) : "memory");
   return v;
-}
-
-// Expert of tile tau: the last e with tpre[e] <= tau (experts without tiles
-// have tpre[e] == tpre[e + 1] and are skipped by this rule).
-__device__ __forceinline__ int expert_of_tile(const int* tpre, int E, int tau) {
-  int lo = 0, hi = E;               // tpre[lo] <= tau < tpre[hi]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (tpre[mid] <= tau) lo = mid;
-    else hi = mid;
-  }
-  return lo;
 }
 
 // Row (within the whole weight tensor) of unit row u (0..255) of column block
@@ -165,39 +152,52 @@ __global__ __launch_bounds__(kThreadsDec) void k_decode(
   const int r16 = lane & 15, g = lane >> 4;
   const int nblk = K / 32;
   const int S = 4 * (K / kChunkK);                 // stages per unit
-  int* offs = reinterpret_cast<int*>(lds + kLdsOffs);
-  int* tpre = reinterpret_cast<int*>(lds + kLdsTpre);
+  int* wsum = reinterpret_cast<int*>(lds + kLdsWsum);
   int4v* units = reinterpret_cast<int4v*>(lds + kLdsUnits);
 
-  // ---- set-up: expert offsets, tiles per expert, the run's unit table
-  for (int i = tid; i <= E; i += kThreadsDec) offs[i] = offsets[i];
-  __syncthreads();
-  if (wave == 0) {
-    int base = 0;
-    for (int c0 = 0; c0 < E; c0 += kWave) {
-      const int e = c0 + lane;
-      int cnt = e < E ? offs[e + 1] - offs[e] : 0;
-      if (cnt < 1 || cnt >= hi) cnt = 0;
-      const int nt = (cnt + kTokRows - 1) / kTokRows;
-      const int incl = wave_incl_scan(nt);
-      if (e < E) tpre[e] = base + incl - nt;
-      base += __shfl(incl, kWave - 1);
-    }
-    if (lane == 0) tpre[E] = base;
+  // ---- set-up: thread t owns experts 2t and 2t + 1; their tiles, one
+  // workgroup-wide scan over experts, then each thread writes the units of
+  // its own tiles that fall in this workgroup's run
+  const int ea = 2 * tid;
+  int off[3] = {0, 0, 0};
+  if (ea < E) {
+    off[0] = offsets[ea];
+    off[1] = offsets[ea + 1];
+    if (ea + 1 < E) off[2] = offsets[ea + 2];
   }
+  int cnt[2], nt[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    cnt[i] = ea + i < E ? off[i + 1] - off[i] : 0;
+    if (cnt[i] < 1 || cnt[i] >= hi) cnt[i] = 0;
+    nt[i] = (cnt[i] + kTokRows - 1) / kTokRows;
+  }
+  const int incl = wave_incl_scan(nt[0] + nt[1]);
+  if (lane == kWave - 1) wsum[wave] = incl;
   __syncthreads();
+  int before = 0, tiles = 0;
+#pragma unroll
+  for (int v = 0; v < kThreadsDec / kWave; ++v) {
+    const int ws = wsum[v];
+    before += v < wave ? ws : 0;
+    tiles += ws;
+  }
   const int G = gridDim.x;
-  const int U = tpre[E] * ntile_n;
+  const int U = tiles * ntile_n;
   const int u0 = __builtin_amdgcn_readfirstlane(int((int64_t(U) * blockIdx.x) / G));
   const int u1 = __builtin_amdgcn_readfirstlane(int((int64_t(U) * (blockIdx.x + 1)) / G));
   const int nu = u1 - u0;
-  for (int idx = tid; idx < nu; idx += kThreadsDec) {
-    const int u = u0 + idx;
-    const int tau = u / ntile_n;
-    const int e = expert_of_tile(tpre, E, tau);
-    const int ti = tau - tpre[e];
-    const int row0 = offs[e] + ti * kTokRows;
-    units[idx] = int4v{e, u - tau * ntile_n, row0, min(kTokRows, offs[e + 1] - row0)};
+  int tfirst = before + incl - nt[0] - nt[1];    // first tile of expert ea
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int ulo = max(u0, tfirst * ntile_n), uhi = min(u1, (tfirst + nt[i]) * ntile_n);
+    for (int u = ulo; u < uhi; ++u) {
+      const int tau = u / ntile_n;
+      const int ti = tau - tfirst;
+      const int row0 = off[i] + ti * kTokRows;
+      units[u - u0] = int4v{ea + i, u - tau * ntile_n, row0, min(kTokRows, cnt[i] - ti * kTokRows)};
+    }
+    tfirst += nt[i];
   }
   __syncthreads();
   const int Q = nu * S;                            // stages of the run
