@@ -1,7 +1,7 @@
 """Benchmark of the MXFP4 MoE expert layer on one MI355X.
 
-One step = the whole layer (moe_route_topk -> moe_permute ->
-moe_mxfp4_gate_up_swiglu -> moe_mxfp4_down -> moe_combine) over one batch of
+One step = the whole layer (moe_route_permute (top-k routing and grouping by
+expert) -> moe_mxfp4_gate_up_swiglu -> moe_mxfp4_down -> moe_combine) over one batch of
 synthetic tokens, inputs resident in HBM.  Default workload: the page-shaped
 layer (hidden 6144, 384 experts, top-8, intermediate 2048, MXFP4 block 32)
 verifying one sequence's 8-token draft block.  Two copies of the expert
@@ -370,9 +370,8 @@ def main():
 
     def step(i, ev=None):
         w = wsets[i & 1]
-        mm.moe_route_topk(logits, k, b.topk_ids, b.topk_w)
-        mm.moe_permute(b.topk_ids, E, b.counts, b.offsets, b.sorted_pairs, b.pair_to_row,
-                       b.workspace)
+        mm.moe_route_permute(logits, k, b.topk_ids, b.topk_w, b.counts, b.offsets,
+                             b.sorted_pairs, b.pair_to_row, b.workspace)
         if ev is not None:
             ev[0].record(stream)
         mm.moe_mxfp4_gate_up_swiglu(x, b.sorted_pairs, b.offsets, k, w["w13_codes"],
@@ -416,24 +415,22 @@ def main():
     tokens_per_s = T / (ms_step * 1e-3)
 
     if args.breakdown:
-        names_k = ("route", "permute", "gate_up", "down", "combine")
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(20)]
+        names_k = ("route+permute", "gate_up", "down", "combine")
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(20)]
         for r in range(20):
             w = wsets[r & 1]
             e = ev[r]
             e[0].record(stream)
-            mm.moe_route_topk(logits, k, b.topk_ids, b.topk_w)
+            mm.moe_route_permute(logits, k, b.topk_ids, b.topk_w, b.counts, b.offsets,
+                                 b.sorted_pairs, b.pair_to_row, b.workspace)
             e[1].record(stream)
-            mm.moe_permute(b.topk_ids, E, b.counts, b.offsets, b.sorted_pairs, b.pair_to_row,
-                           b.workspace)
-            e[2].record(stream)
             mm.moe_mxfp4_gate_up_swiglu(x, b.sorted_pairs, b.offsets, k, w["w13_codes"],
                                         w["w13_scales"], b.h)
-            e[3].record(stream)
+            e[2].record(stream)
             mm.moe_mxfp4_down(b.h, b.offsets, k, w["w2_codes"], w["w2_scales"], b.y)
-            e[4].record(stream)
+            e[3].record(stream)
             mm.moe_combine(b.y, b.topk_w, b.pair_to_row, b.out)
-            e[5].record(stream)
+            e[4].record(stream)
         torch.cuda.synchronize()
         for i, n in enumerate(names_k):
             t = np.median([ev[r][i].elapsed_time(ev[r][i + 1]) for r in range(20)])

@@ -192,6 +192,20 @@ int moe_permute(const int32_t* topk_ids, int T, int E, int k,
                 void* stream);
 
 /*
+ * moe_route_permute — moe_route_topk followed by moe_permute, in one call.
+ *   arguments as those two calls (topk_ids and topk_w are written, then read)
+ * Results are bit-identical to the two calls.  For T <= 16 (and E small
+ * enough that the grouping tables fit 64 KB of LDS) both steps run in one
+ * workgroup, the ids passing through LDS: one launch and one round trip to
+ * memory fewer, which is most of their cost at decode sizes.  Errors as the
+ * two calls; nothing is enqueued on a shape, null-pointer or alignment error.
+ */
+int moe_route_permute(const float* logits, int T, int E, int k, int32_t* topk_ids,
+                      float* topk_w, int32_t* counts, int32_t* offsets, int32_t* sorted_pairs,
+                      int32_t* pair_to_row, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/*
  * moe_mxfp4_gate_up_swiglu — first half of every chosen expert's FFN.
  *   x_bf16       [T, H] bf16 activations, read
  *   sorted_pairs [T*k], offsets [E+1] from moe_permute, read

@@ -7,7 +7,7 @@ and the current stream) into those calls; see `ops`."""
 from . import _lib  # noqa: F401
 from .ops import (  # noqa: F401
     LayerBuffers, dflash_verify_accept, moe_combine, moe_mxfp4_down, moe_mxfp4_gate_up_swiglu, moe_mxfp4_layer,
-    moe_permute, moe_permute_workspace_bytes, moe_route_topk, moe_router_topk, mxfp4_pack,
+    moe_permute, moe_permute_workspace_bytes, moe_route_permute, moe_route_topk, moe_router_topk, mxfp4_pack,
     mxfp4_unpack,
 )
 

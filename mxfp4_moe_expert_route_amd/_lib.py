@@ -24,6 +24,8 @@ SIGNATURES = {
                                       _p]),
     "moe_permute_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int]),
     "moe_permute": (_c_int, [_p, _c_int, _c_int, _c_int, _p, _p, _p, _p, _p, _c_size, _p]),
+    "moe_route_permute": (_c_int, [_p, _c_int, _c_int, _c_int, _p, _p, _p, _p, _p, _p, _p,
+                                   _c_size, _p]),
     "moe_mxfp4_gate_up_swiglu": (_c_int, [_p, _p, _p, _c_int, _c_int, _c_int, _c_int, _c_int,
                                           _p, _p, _p, _p]),
     "moe_mxfp4_down": (_c_int, [_p, _p, _c_int, _c_int, _c_int, _c_int, _c_int, _p, _p, _p, _p]),

@@ -164,6 +164,30 @@ int moe_permute(const int32_t* topk_ids, int T, int E, int k, int32_t* counts, i
                                       pair_to_row, as_stream(stream)));
 }
 
+int moe_route_permute(const float* logits, int T, int E, int k, int32_t* topk_ids,
+                      float* topk_w, int32_t* counts, int32_t* offsets, int32_t* sorted_pairs,
+                      int32_t* pair_to_row, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  const int st = check_route_shape(T, E, k);
+  if (st != MXM_OK) return st;
+  if (workspace_bytes < moe_permute_workspace_bytes(T, E, k)) return MXM_ERR_WORKSPACE;
+  if (T == 0) return MXM_OK;
+  if (!logits || !topk_ids || !topk_w || !counts || !offsets || !sorted_pairs || !pair_to_row)
+    return MXM_ERR_NULL;
+  if (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4) ||
+      !aligned(counts, 4) || !aligned(offsets, 4) || !aligned(sorted_pairs, 4) ||
+      !aligned(pair_to_row, 4))
+    return MXM_ERR_ALIGN;
+  const hipStream_t s = as_stream(stream);
+  if (mxm::route_permute_fusable(T, E, k))
+    return launched(mxm::launch_route_permute(logits, T, E, k, topk_ids, topk_w, counts, offsets,
+                                              sorted_pairs, pair_to_row, s));
+  if (mxm::launch_route_topk(logits, T, E, k, topk_ids, topk_w, s) != hipSuccess)
+    return MXM_ERR_LAUNCH;
+  return launched(mxm::launch_permute(topk_ids, T, E, k, counts, offsets, sorted_pairs,
+                                      pair_to_row, s));
+}
+
 int moe_mxfp4_gate_up_swiglu(const uint16_t* x_bf16, const int32_t* sorted_pairs,
                              const int32_t* offsets, int T, int H, int I, int E, int k,
                              const uint8_t* w13_codes, const uint8_t* w13_scales,
@@ -239,9 +263,8 @@ int moe_mxfp4_layer(const uint16_t* x_bf16, const float* logits, int T, int H, i
       !aligned(topk_ids, 4) || !aligned(topk_w, 4) || !aligned(counts, 4) ||
       !aligned(offsets, 4) || !aligned(sorted_pairs, 4) || !aligned(pair_to_row, 4))
     return MXM_ERR_ALIGN;
-  if ((st = moe_route_topk(logits, T, E, k, topk_ids, topk_w, stream)) != MXM_OK) return st;
-  if ((st = moe_permute(topk_ids, T, E, k, counts, offsets, sorted_pairs, pair_to_row, workspace,
-                        workspace_bytes, stream)) != MXM_OK)
+  if ((st = moe_route_permute(logits, T, E, k, topk_ids, topk_w, counts, offsets, sorted_pairs,
+                              pair_to_row, workspace, workspace_bytes, stream)) != MXM_OK)
     return st;
   if ((st = moe_mxfp4_gate_up_swiglu(x_bf16, sorted_pairs, offsets, T, H, I, E, k, w13_codes,
                                      w13_scales, h_bf16, stream)) != MXM_OK)

@@ -113,6 +113,12 @@ hipError_t launch_pack(const void* x, int x_dtype, int64_t rows, int64_t K, uint
                        uint8_t* scales, hipStream_t s);
 hipError_t launch_unpack(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t K,
                          void* y, int y_dtype, hipStream_t s);
+// routing and grouping in one workgroup, for T <= 16 (same results as the
+// two launches below)
+bool route_permute_fusable(int T, int E, int k);
+hipError_t launch_route_permute(const float* logits, int T, int E, int k, int32_t* ids, float* w,
+                                int32_t* counts, int32_t* offsets, int32_t* sorted_pairs,
+                                int32_t* pair_to_row, hipStream_t s);
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
                              hipStream_t s);
 hipError_t launch_router_logits(const uint16_t* x, const float* w_router, const float* bias, int T,

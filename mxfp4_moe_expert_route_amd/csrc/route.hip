@@ -1,71 +1,13 @@
-// Top-k routing (one wave64 per token) and the router projection in front of
-// it.
-//
-// The pages give 384 experts with 8 active per token (nxbn.cn article,
-// "架构设计与配置详解") and no scoring rule.  Rule used (a reading): experts by
-// descending logit, lower index first on equal logits, -0.0 == +0.0, NaN as
-// -inf; weights = softmax over all experts renormalised over the chosen k,
-// which equals exp(l_j - l_1) / sum_j' exp(l_j' - l_1) over the chosen.
-//
-// Each logit becomes a 64-bit key: an order-preserving 32-bit image of the
-// float in the high word and (0xffffffff - index) in the low word, so the
-// unsigned maximum is the largest logit with the lowest index.  k rounds of a
-// wave-wide max (per-lane max, then DPP row shifts and row broadcasts) pick
-// the experts; the picked key is cleared to 0, below every valid key.
-#include "common.hpp"
+// Top-k routing (one wave64 per token), the same fused with the grouping of
+// pairs by expert for small batches, and the router projection in front of
+// them.  The top-k rule, its key encoding and the grouping are in
+// routing.hpp.
+#include "routing.hpp"
 
 namespace mxm {
 namespace {
 
-__device__ __forceinline__ uint32_t order_key(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) u = 0xff800000u;   // NaN ranks as -inf
-  if (u == 0x80000000u) u = 0u;                            // -0.0 ties with +0.0
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-__device__ __forceinline__ float key_value(uint32_t key) {
-  return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
-}
-
-__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
-
-// v moved across lanes by the DPP control CTRL (rows and banks masked by
-// RM); lanes whose source is outside the row read 0, below every key
-template <int CTRL, int RM>
-__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
-  const int lo = __builtin_amdgcn_update_dpp(0, int(uint32_t(v)), CTRL, RM, 0xf, true);
-  const int hi = __builtin_amdgcn_update_dpp(0, int(uint32_t(v >> 32)), CTRL, RM, 0xf, true);
-  return (uint64_t(uint32_t(hi)) << 32) | uint32_t(lo);
-}
-
-// Largest key of the wave, in every lane.  Row shifts build each 16-lane
-// row's maximum in its lane 15, two row broadcasts carry them to lane 63;
-// DPP keeps the whole reduction in the VALU (no LDS round trips).
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-  v = max_u64(v, dpp_u64<0x111, 0xf>(v));   // row_shr:1
-  v = max_u64(v, dpp_u64<0x112, 0xf>(v));   // row_shr:2
-  v = max_u64(v, dpp_u64<0x114, 0xf>(v));   // row_shr:4
-  v = max_u64(v, dpp_u64<0x118, 0xf>(v));   // row_shr:8
-  v = max_u64(v, dpp_u64<0x142, 0xa>(v));   // row_bcast:15 into rows 1 and 3
-  v = max_u64(v, dpp_u64<0x143, 0xc>(v));   // row_bcast:31 into rows 2 and 3
-  const uint32_t lo = __builtin_amdgcn_readlane(int(uint32_t(v)), kWave - 1);
-  const uint32_t hi = __builtin_amdgcn_readlane(int(uint32_t(v >> 32)), kWave - 1);
-  return (uint64_t(hi) << 32) | lo;
-}
-
-// Sum over the wave in a fixed order (the same reduction tree as above), in
-// every lane.
-__device__ __forceinline__ float wave_sum_f32(float v) {
-  auto add = [&](float x, int y) { return x + __int_as_float(y); };
-  v = add(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xf, 0xf, true));
-  v = add(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xf, 0xf, true));
-  v = add(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xf, 0xf, true));
-  v = add(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xf, 0xf, true));
-  v = add(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xa, 0xf, true));
-  v = add(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xc, 0xf, true));
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), kWave - 1));
-}
+constexpr int kFusedWaves = 16;
 
 template <int NPER>
 __global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ logits, int T,
@@ -74,35 +16,53 @@ __global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ lo
   const int t = int((int64_t(blockIdx.x) * blockDim.x + threadIdx.x) >> 6);
   if (t >= T) return;                                      // whole wave leaves together
   const int lane = lane_id();
-  const float* row = logits + int64_t(t) * E;
-  uint64_t key[NPER];
-#pragma unroll
-  for (int i = 0; i < NPER; ++i) {
-    const int e = lane + kWave * i;
-    key[i] = (e < E) ? (uint64_t(order_key(row[e])) << 32) | uint64_t(0xffffffffu - uint32_t(e))
-                     : 0ull;
-  }
-  int my_id = 0;
-  float my_l = 0.f, l1 = 0.f;
-  for (int j = 0; j < k; ++j) {
-    uint64_t best = key[0];
-#pragma unroll
-    for (int i = 1; i < NPER; ++i) best = max_u64(best, key[i]);
-    best = wave_max_u64(best);
-#pragma unroll
-    for (int i = 0; i < NPER; ++i) key[i] = (key[i] == best) ? 0ull : key[i];
-    if (j == 0) l1 = key_value(uint32_t(best >> 32));
-    if (lane == j) {
-      my_id = int(0xffffffffu - uint32_t(best));
-      my_l = key_value(uint32_t(best >> 32));
-    }
-  }
-  const float ex = (lane < k) ? expf(my_l - l1) : 0.f;
-  const float sum = wave_sum_f32(ex);
+  int my_id;
+  float my_w;
+  route_token<NPER>(logits + int64_t(t) * E, E, k, my_id, my_w);
   if (lane < k) {
     ids[int64_t(t) * k + lane] = my_id;
-    w[int64_t(t) * k + lane] = ex / sum;
+    w[int64_t(t) * k + lane] = my_w;
   }
+}
+
+// Small batches (T <= 16): routing and grouping in one workgroup of 16 waves.
+// Wave t routes token t; the ids go to global memory and to LDS, and after
+// one barrier the workgroup groups the pairs from LDS.  Same functions as the
+// two separate kernels, so the same results; one launch and one round trip
+// to memory fewer.
+template <int NPER>
+__global__ __launch_bounds__(kFusedWaves * kWave) void k_route_permute(
+    const float* __restrict__ logits, int T, int E, int k, int32_t* __restrict__ ids,
+    float* __restrict__ w, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ pair_to_row) {
+  extern __shared__ int32_t smem[];            // permutation tables, then the ids
+  __shared__ int32_t wave_sum[kFusedWaves];
+  int32_t* lds_ids = smem + (kFusedWaves + 1) * E;
+  const int t = threadIdx.x >> 6;
+  const int lane = lane_id();
+  if (t < T) {
+    int my_id;
+    float my_w;
+    route_token<NPER>(logits + int64_t(t) * E, E, k, my_id, my_w);
+    if (lane < k) {
+      ids[int64_t(t) * k + lane] = my_id;
+      w[int64_t(t) * k + lane] = my_w;
+      lds_ids[t * k + lane] = my_id;
+    }
+  }
+  __syncthreads();
+  permute_block<kFusedWaves>(lds_ids, T * k, E, counts, offsets, sorted_pairs, pair_to_row, smem,
+                             wave_sum);
+}
+
+template <int NPER>
+hipError_t launch_fused_n(const float* logits, int T, int E, int k, int32_t* ids, float* w,
+                          int32_t* counts, int32_t* offsets, int32_t* sorted_pairs,
+                          int32_t* pair_to_row, hipStream_t s) {
+  const size_t lds = (size_t(kFusedWaves + 1) * E + size_t(T) * k) * sizeof(int32_t);
+  k_route_permute<NPER><<<1, kFusedWaves * kWave, lds, s>>>(logits, T, E, k, ids, w, counts,
+                                                            offsets, sorted_pairs, pair_to_row);
+  return hipGetLastError();
 }
 
 template <int NPER>
@@ -304,6 +264,22 @@ hipError_t launch_router_logits(const uint16_t* x, const float* w_router, const 
     k_router_tiles<32, 32><<<grid, 256, 0, s>>>(x, w_router, bias, T, H, E, logits);
   }
   return hipGetLastError();
+}
+
+bool route_permute_fusable(int T, int E, int k) {
+  return T >= 1 && T <= kFusedWaves &&
+         (size_t(kFusedWaves + 1) * E + size_t(T) * k) * sizeof(int32_t) <= 64 * 1024;
+}
+
+hipError_t launch_route_permute(const float* logits, int T, int E, int k, int32_t* ids, float* w,
+                                int32_t* counts, int32_t* offsets, int32_t* sorted_pairs,
+                                int32_t* pair_to_row, hipStream_t s) {
+  const int nper = (E + kWave - 1) / kWave;
+  if (nper <= 1) return launch_fused_n<1>(logits, T, E, k, ids, w, counts, offsets, sorted_pairs, pair_to_row, s);
+  if (nper <= 2) return launch_fused_n<2>(logits, T, E, k, ids, w, counts, offsets, sorted_pairs, pair_to_row, s);
+  if (nper <= 4) return launch_fused_n<4>(logits, T, E, k, ids, w, counts, offsets, sorted_pairs, pair_to_row, s);
+  if (nper <= 8) return launch_fused_n<8>(logits, T, E, k, ids, w, counts, offsets, sorted_pairs, pair_to_row, s);
+  return launch_fused_n<16>(logits, T, E, k, ids, w, counts, offsets, sorted_pairs, pair_to_row, s);
 }
 
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,

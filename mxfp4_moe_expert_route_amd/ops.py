@@ -154,6 +154,30 @@ def moe_permute(topk_ids, E, counts=None, offsets=None, sorted_pairs=None, pair_
     return counts, offsets, sorted_pairs, pair_to_row
 
 
+def moe_route_permute(logits, k, topk_ids=None, topk_w=None, counts=None, offsets=None,
+                      sorted_pairs=None, pair_to_row=None, workspace=None):
+    """logits [T, E] f32 -> (topk_ids [T, k], topk_w [T, k], counts [E], offsets [E+1],
+    sorted_pairs [T*k], pair_to_row [T*k]); moe_route_topk then moe_permute in one call."""
+    _need(logits, "logits", torch.float32)
+    T, E = logits.shape
+    dev = logits.device
+    topk_ids = _out(topk_ids, "topk_ids", torch.int32, (T, k), dev)
+    topk_w = _out(topk_w, "topk_w", torch.float32, (T, k), dev)
+    counts = _out(counts, "counts", torch.int32, (E,), dev)
+    offsets = _out(offsets, "offsets", torch.int32, (E + 1,), dev)
+    sorted_pairs = _out(sorted_pairs, "sorted_pairs", torch.int32, (T * k,), dev)
+    pair_to_row = _out(pair_to_row, "pair_to_row", torch.int32, (T * k,), dev)
+    nws = moe_permute_workspace_bytes(T, E, k)
+    if workspace is None and nws:
+        workspace = torch.empty(nws, dtype=torch.uint8, device=dev)
+    wsb = workspace.numel() if workspace is not None else 0
+    check(lib().moe_route_permute(_ptr(logits), T, E, k, _ptr(topk_ids), _ptr(topk_w),
+                                  _ptr(counts), _ptr(offsets), _ptr(sorted_pairs),
+                                  _ptr(pair_to_row), _ptr(workspace), wsb, _stream()),
+          "moe_route_permute")
+    return topk_ids, topk_w, counts, offsets, sorted_pairs, pair_to_row
+
+
 def moe_mxfp4_gate_up_swiglu(x, sorted_pairs, offsets, k, w13_codes, w13_scales, h=None):
     """x [T, H] bf16 -> h [T*k, I] bf16 (rows in sorted order)."""
     _need(x, "x", torch.bfloat16)

@@ -31,7 +31,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("mxfp4_pack", "mxfp4_unpack", "moe_route_topk", "moe_router_topk",
               "dflash_verify_accept", "dflash_verify_workspace_bytes", "moe_permute",
-              "moe_permute_workspace_bytes", "moe_mxfp4_gate_up_swiglu", "moe_mxfp4_down",
+              "moe_permute_workspace_bytes", "moe_route_permute", "moe_mxfp4_gate_up_swiglu", "moe_mxfp4_down",
               "moe_combine", "moe_mxfp4_layer", "mxm_status_string", "mxm_version"):
         assert n in names
 
@@ -72,6 +72,12 @@ def test_route_permute_argument_checks(lib):
     assert lib.moe_route_topk(P, 4, 8, 0, P, P, None) == -2
     assert lib.moe_route_topk(None, 4, 8, 2, P, P, None) == -1
     assert lib.moe_route_topk(P + 2, 4, 8, 2, P, P, None) == -4
+    assert lib.moe_route_permute(P, 4, 8, 9, P, P, P, P, P, P, None, 0, None) == -2   # k > E
+    assert lib.moe_route_permute(P, 4, 1025, 8, P, P, P, P, P, P, None, 0, None) == -2
+    assert lib.moe_route_permute(P, 4, 8, 2, P, P, None, P, P, P, None, 0, None) == -1
+    assert lib.moe_route_permute(P, 4, 8, 2, P, P, P, P + 2, P, P, None, 0, None) == -4
+    assert lib.moe_route_permute(P, 0, 8, 2, None, None, None, None, None, None, None, 0,
+                                 None) == 0
     assert lib.moe_route_topk(None, 0, 8, 2, None, None, None) == 0
     assert lib.moe_permute_workspace_bytes(64, 384, 8) == 0
     assert lib.moe_permute(P, 4, 8, 2, P, P, P, None, None, 0, None) == -1

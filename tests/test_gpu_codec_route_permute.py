@@ -190,3 +190,35 @@ def test_permute_edge_shapes(mm, T, E, k, mode):
     else:
         ids = np.stack([rng.permutation(E)[:k] for _ in range(T)])
     check_permute(mm, ids, E)
+
+
+# ---------------------------------------------------------------------------
+# routing and grouping in one call (one fused workgroup up to 16 tokens)
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 1, 1), (1, 64, 8), (8, 384, 8), (9, 65, 21), (16, 960, 32),
+                                   (16, 384, 8), (17, 384, 8), (64, 1024, 32)])
+def test_route_permute_matches_oracle_and_two_calls(mm, T, E, k):
+    rng = np.random.default_rng(T * 7 + E * 31 + k)
+    pool = np.array([0.0, -0.0, 1.5, -2.0, 3.25, 0.5, -math.inf, math.nan], np.float32)
+    l = rng.choice(pool, size=(T, E)).astype(np.float32)
+    l[: (T + 1) // 2] = rng.standard_normal(((T + 1) // 2, E)).astype(np.float32)
+    ld = torch.from_numpy(l).to(DEV)
+    got = mm.moe_route_permute(ld, k)
+    ids2, w2 = mm.moe_route_topk(ld, k)
+    lists2 = mm.moe_permute(ids2, E)
+    torch.cuda.synchronize()
+    ri, rw = oroute.route_topk(l, k)
+    ref = operm.permute(ri, E)
+    assert np.array_equal(got[0].cpu().numpy(), ri)
+    wg = got[1].cpu().numpy()
+    fin = np.isfinite(rw)
+    assert np.array_equal(np.isfinite(wg), fin)
+    assert np.abs(wg[fin].astype(np.float64) - rw[fin]).max(initial=0) <= W_ATOL
+    for name, g in zip(("counts", "offsets", "sorted_pairs", "pair_to_row"), got[2:]):
+        assert np.array_equal(g.cpu().numpy(), ref[name]), name
+    # bit-identical to the two separate calls, weights included
+    assert torch.equal(got[0], ids2)
+    assert torch.equal(got[1].view(torch.int32), w2.view(torch.int32))
+    for g, g2 in zip(got[2:], lists2):
+        assert torch.equal(g, g2)

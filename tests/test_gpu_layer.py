@@ -28,6 +28,7 @@ SMALL = [
     ("min_dims", (9, 32, 32, 3, 2)),           # one MX block per row
     ("many_e", (64, 256, 64, 1024, 32)),       # most experts empty
     ("wide_k", (300, 2048, 512, 32, 8)),
+    ("fused_e960", (16, 256, 64, 960, 32)),   # routing and grouping fused (T <= 16), largest E
 ]
 
 # shapes that take the LDS-tiled dense kernel (H, I multiples of 512, many
@@ -71,6 +72,22 @@ def test_layer_small_every_token(mm, name, shape):
     say("layer", name, cfg)
     d = workloads.layer_inputs(cfg, 0)
     check_layer(cfg, d["x_bits"], d["logits"], d, upload_weights(d))
+
+
+def test_layer_fused_routing_ties(mm):
+    """Up to 16 tokens are routed and grouped by one fused workgroup: integer
+    logits (many ties), -0.0 next to +0.0 and NaN rows give the oracle's ids
+    and lists bit for bit."""
+    cfg = workloads.custom_config("fused_ties", 603, 12, 256, 64, 40, 6)
+    say("layer", cfg.name, cfg)
+    d = workloads.layer_inputs(cfg, 0)
+    rng = np.random.default_rng(603)
+    lg = rng.integers(-3, 4, size=(cfg.T, cfg.E)).astype(np.float32)
+    lg[0, 5], lg[0, 6] = -0.0, 0.0
+    lg[1, :] = np.nan
+    lg[1, 7] = 1.0
+    lg[2, 3] = np.nan
+    check_layer(cfg, d["x_bits"], lg, d, upload_weights(d))
 
 
 @pytest.mark.parametrize("name,shape,routing", DENSE, ids=[d[0] for d in DENSE])
