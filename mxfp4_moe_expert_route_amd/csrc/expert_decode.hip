@@ -279,25 +279,41 @@ __global__ __launch_bounds__(kThreadsDec) void k_decode(
   if (wave >= kMW) {
     // ---------------- code loaders ----------------
     const int ld = wave - kMW;
-    int cur = -1;
-    int4v ui{0, 0, 0, 1};
-    auto issue = [&](int p) {
-      const int j = p / S, s = p - j * S;
+    // The loads of a stage go out right after its barrier and their issue
+    // is on the critical path of the stream: each lane's offsets within a
+    // row group are fixed, so only a scalar base changes per stage (the
+    // weight rows of a row group are consecutive: I % 128 == 0 and
+    // H % 256 == 0 keep weight_row from clamping).  Measured: 150.0 ->
+    // 147.7 us for 4 gate/up units per workgroup.
+    int cur = -1, j = 0, s = 0;
+    // per lane, the byte offset of load m within a row group's first chunk
+    uint32_t loff[kPerLoader];
+#pragma unroll
+    for (int m = 0; m < kPerLoader; ++m) {
+      const int i = ld + kCW * m;
+      const int rr = 4 * i + (lane >> 4);
+      loff[m] = uint32_t(rr) * uint32_t(K / 2) + uint32_t(((lane & 15) ^ (rr & 15)) * 16);
+    }
+    const uint8_t* ubase[4];                       // first byte of each row group of the unit
+    auto issue = [&](int p) {                      // p = j S + s
       if (j != cur) {
         cur = j;
-        ui = lds_read_i32x4(lds + kLdsUnits + 16 * j);
+        const int4v ui = lds_read_i32x4(lds + kLdsUnits + 16 * j);
+        const int ex = __builtin_amdgcn_readfirstlane(ui.x), nt = __builtin_amdgcn_readfirstlane(ui.y);
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg)
+          ubase[rg] = codes + weight_row<GU>(ex, nt, kGroupRows * rg, I, H) * (K / 2);
       }
       const int kc = s >> 2, rg = s & 3;
+      const uint8_t* b = (rg == 0 ? ubase[0] : rg == 1 ? ubase[1] : rg == 2 ? ubase[2] : ubase[3]) +
+                         kc * (kChunkK / 2);
       uint8_t* st = lds + (p % kRing) * kStageB;
 #pragma unroll
-      for (int m = 0; m < kPerLoader; ++m) {
-        const int i = ld + kCW * m;                // load i: rows 4i..4i+3 of the group
-        const int rr = 4 * i + (lane >> 4);
-        const int blk = (lane & 15) ^ (rr & 15);
-        const uint8_t* src = codes +
-                             weight_row<GU>(ui.x, ui.y, kGroupRows * rg + rr, I, H) * (K / 2) +
-                             kc * (kChunkK / 2) + blk * 16;
-        __builtin_amdgcn_global_load_lds(src, lds_at(st, i * 1024), 16, 0, 0);
+      for (int m = 0; m < kPerLoader; ++m)
+        __builtin_amdgcn_global_load_lds(b + loff[m], lds_at(st, (ld + kCW * m) * 1024), 16, 0, 0);
+      if (++s == S) {
+        s = 0;
+        ++j;
       }
     };
     for (int p = 0; p < pre; ++p) issue(p);
