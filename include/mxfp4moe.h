@@ -168,7 +168,10 @@ int dflash_verify_accept(const float* target_logits, const float* draft_probs,
                          int V, int32_t* accept_len, int32_t* next_token, void* workspace,
                          size_t workspace_bytes, void* stream);
 
-/* Workspace moe_permute needs for these sizes (currently always 0). */
+/* Workspace moe_permute (and moe_route_permute, moe_mxfp4_layer) needs for
+ * these sizes: 0 up to 8192 pairs (T*k), above that 4*E bytes per range of
+ * 1024 pairs (at most 1024 ranges): per-range histograms, then per-range
+ * bases.  0 for invalid sizes. */
 size_t moe_permute_workspace_bytes(int T, int E, int k);
 
 /*
@@ -180,7 +183,8 @@ size_t moe_permute_workspace_bytes(int T, int E, int k);
  *                in expert order, ascending p within a segment
  *   pair_to_row  [T*k] int32, written: inverse of sorted_pairs
  *   workspace    device scratch of moe_permute_workspace_bytes(T, E, k)
- *                bytes (may be NULL when that is 0)
+ *                bytes, 4-byte aligned (may be NULL when that is 0); its
+ *                contents need no initialisation and are overwritten
  * Bookkeeping the grouped expert contractions need; not on the pages.
  * Bit-exact and deterministic.  A pair whose id is outside [0, E) is
  * dropped: it is not counted, its pair_to_row entry is -1 and offsets[E]

@@ -142,10 +142,8 @@ int dflash_verify_accept(const float* target_logits, const float* draft_probs,
 }
 
 size_t moe_permute_workspace_bytes(int T, int E, int k) {
-  (void)T;
-  (void)E;
-  (void)k;
-  return 0;
+  if (check_route_shape(T, E, k) != MXM_OK) return 0;
+  return mxm::permute_workspace_bytes(T, E, k);
 }
 
 int moe_permute(const int32_t* topk_ids, int T, int E, int k, int32_t* counts, int32_t* offsets,
@@ -154,14 +152,14 @@ int moe_permute(const int32_t* topk_ids, int T, int E, int k, int32_t* counts, i
   const int st = check_route_shape(T, E, k);
   if (st != MXM_OK) return st;
   if (workspace_bytes < moe_permute_workspace_bytes(T, E, k)) return MXM_ERR_WORKSPACE;
-  (void)workspace;
   if (T == 0) return MXM_OK;
   if (!topk_ids || !counts || !offsets || !sorted_pairs || !pair_to_row) return MXM_ERR_NULL;
+  if (moe_permute_workspace_bytes(T, E, k) > 0 && !workspace) return MXM_ERR_NULL;
   if (!aligned(topk_ids, 4) || !aligned(counts, 4) || !aligned(offsets, 4) ||
-      !aligned(sorted_pairs, 4) || !aligned(pair_to_row, 4))
+      !aligned(sorted_pairs, 4) || !aligned(pair_to_row, 4) || !aligned(workspace, 4))
     return MXM_ERR_ALIGN;
   return launched(mxm::launch_permute(topk_ids, T, E, k, counts, offsets, sorted_pairs,
-                                      pair_to_row, as_stream(stream)));
+                                      pair_to_row, workspace, as_stream(stream)));
 }
 
 int moe_route_permute(const float* logits, int T, int E, int k, int32_t* topk_ids,
@@ -174,9 +172,10 @@ int moe_route_permute(const float* logits, int T, int E, int k, int32_t* topk_id
   if (T == 0) return MXM_OK;
   if (!logits || !topk_ids || !topk_w || !counts || !offsets || !sorted_pairs || !pair_to_row)
     return MXM_ERR_NULL;
+  if (moe_permute_workspace_bytes(T, E, k) > 0 && !workspace) return MXM_ERR_NULL;
   if (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4) ||
       !aligned(counts, 4) || !aligned(offsets, 4) || !aligned(sorted_pairs, 4) ||
-      !aligned(pair_to_row, 4))
+      !aligned(pair_to_row, 4) || !aligned(workspace, 4))
     return MXM_ERR_ALIGN;
   const hipStream_t s = as_stream(stream);
   if (mxm::route_permute_fusable(T, E, k))
@@ -185,7 +184,7 @@ int moe_route_permute(const float* logits, int T, int E, int k, int32_t* topk_id
   if (mxm::launch_route_topk(logits, T, E, k, topk_ids, topk_w, s) != hipSuccess)
     return MXM_ERR_LAUNCH;
   return launched(mxm::launch_permute(topk_ids, T, E, k, counts, offsets, sorted_pairs,
-                                      pair_to_row, s));
+                                      pair_to_row, workspace, s));
 }
 
 int moe_mxfp4_gate_up_swiglu(const uint16_t* x_bf16, const int32_t* sorted_pairs,

@@ -9,10 +9,10 @@
 namespace mxm {
 namespace {
 
-// One workgroup per (token, 1024 columns): the token's k rows and weights are
-// read once into LDS, then every thread issues its k row loads together (no
-// branch between them: a dropped pair reads row 0 and its term is not added)
-// and accumulates them in slot order.
+// One workgroup per (token, 2048 columns): the token's k rows and weights are
+// read once into LDS, then every thread issues its 2k row loads together (two
+// float4 per row, 1024 columns apart; no branch between them: a dropped pair
+// reads row 0 and its term is not added) and accumulates them in slot order.
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y,
                                                  const float* __restrict__ w,
                                                  const int32_t* __restrict__ pair_to_row, int T,
@@ -25,36 +25,40 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y,
     sw[threadIdx.x] = w[int64_t(t) * k + threadIdx.x];
   }
   __syncthreads();
-  const int c = blockIdx.y * 1024 + threadIdx.x * 4;
-  if (c >= H) return;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  const int c0 = blockIdx.y * 2048 + threadIdx.x * 4;      // columns c0 and c0 + 1024
+  const bool in1 = c0 + 1024 < H;
+  if (c0 >= H) return;
+  float4 acc0 = make_float4(0.f, 0.f, 0.f, 0.f), acc1 = acc0;
   for (int j0 = 0; j0 < k; j0 += 8) {
-    float4 v[8];
+    float4 v0[8], v1[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int r = (j0 + i < k) ? max(srow[j0 + i], 0) : 0;
-      v[i] = *reinterpret_cast<const float4*>(y + int64_t(r) * H + c);
+      const float* yr = y + int64_t(r) * H + c0;
+      v0[i] = *reinterpret_cast<const float4*>(yr);
+      v1[i] = in1 ? *reinterpret_cast<const float4*>(yr + 1024) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int j = j0 + i;
       if (j < k && srow[j] >= 0) {
         const float wj = sw[j];
-        acc.x = fmaf(wj, v[i].x, acc.x);
-        acc.y = fmaf(wj, v[i].y, acc.y);
-        acc.z = fmaf(wj, v[i].z, acc.z);
-        acc.w = fmaf(wj, v[i].w, acc.w);
+        acc0.x = fmaf(wj, v0[i].x, acc0.x); acc0.y = fmaf(wj, v0[i].y, acc0.y);
+        acc0.z = fmaf(wj, v0[i].z, acc0.z); acc0.w = fmaf(wj, v0[i].w, acc0.w);
+        acc1.x = fmaf(wj, v1[i].x, acc1.x); acc1.y = fmaf(wj, v1[i].y, acc1.y);
+        acc1.z = fmaf(wj, v1[i].z, acc1.z); acc1.w = fmaf(wj, v1[i].w, acc1.w);
       }
     }
   }
-  *reinterpret_cast<float4*>(out + int64_t(t) * H + c) = acc;
+  *reinterpret_cast<float4*>(out + int64_t(t) * H + c0) = acc0;
+  if (in1) *reinterpret_cast<float4*>(out + int64_t(t) * H + c0 + 1024) = acc1;
 }
 
 }  // namespace
 
 hipError_t launch_combine(const float* y, const float* w, const int32_t* pair_to_row, int T,
                           int H, int k, float* out, hipStream_t s) {
-  k_combine<<<dim3(unsigned(T), unsigned((H + 1023) / 1024)), 256, 0, s>>>(y, w, pair_to_row, T,
+  k_combine<<<dim3(unsigned(T), unsigned((H + 2047) / 2048)), 256, 0, s>>>(y, w, pair_to_row, T,
                                                                           H, k, out);
   return hipGetLastError();
 }

@@ -123,9 +123,10 @@ hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* 
                              hipStream_t s);
 hipError_t launch_router_logits(const uint16_t* x, const float* w_router, const float* bias, int T,
                                 int H, int E, float* logits, hipStream_t s);
+size_t permute_workspace_bytes(int T, int E, int k);
 hipError_t launch_permute(const int32_t* ids, int T, int E, int k, int32_t* counts,
                           int32_t* offsets, int32_t* sorted_pairs, int32_t* pair_to_row,
-                          hipStream_t s);
+                          void* workspace, hipStream_t s);
 // Streaming kernels: experts with fewer than `hi` rows (all when hi is INT_MAX).
 hipError_t launch_gate_up(const uint16_t* x, const int32_t* sorted_pairs, const int32_t* offsets,
                           int T, int H, int I, int E, int k, const uint8_t* codes,

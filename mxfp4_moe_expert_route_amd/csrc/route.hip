@@ -51,8 +51,8 @@ __global__ __launch_bounds__(kFusedWaves * kWave) void k_route_permute(
     }
   }
   __syncthreads();
-  permute_block<kFusedWaves>(lds_ids, T * k, E, counts, offsets, sorted_pairs, pair_to_row, smem,
-                             wave_sum);
+  permute_block<kFusedWaves>(lds_ids, 0, T * k, E, nullptr, counts, offsets, sorted_pairs,
+                             pair_to_row, smem, wave_sum);
 }
 
 template <int NPER>

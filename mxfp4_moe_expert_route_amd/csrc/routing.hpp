@@ -122,10 +122,15 @@ __device__ __forceinline__ void route_token(const float* __restrict__ row, int E
 
 constexpr int kBatch = 8;                     // 64-pair groups whose ids load together
 
-// Executed by a whole workgroup of exactly NW waves; smem holds (NW + 1) * E
-// ints and wave_sum NW.  ids may point to global memory or LDS.
+// Executed by a whole workgroup of exactly NW waves over the pairs [r0, r1);
+// smem holds (NW + 1) * E ints and wave_sum NW.  ids may point to global
+// memory or LDS.  With gbase == nullptr the workgroup holds every pair
+// (r0 = 0, r1 = R) and writes counts and offsets; otherwise it is one of
+// several workgroups over consecutive ranges and gbase[e] is the first row of
+// expert e for its range (computed from all ranges' histograms beforehand).
 template <int NW>
-__device__ __forceinline__ void permute_block(const int32_t* ids, int R, int E,
+__device__ __forceinline__ void permute_block(const int32_t* ids, int r0, int r1, int E,
+                                              const int32_t* gbase,
                                               int32_t* __restrict__ counts,
                                               int32_t* __restrict__ offsets,
                                               int32_t* __restrict__ sorted_pairs,
@@ -137,14 +142,15 @@ __device__ __forceinline__ void permute_block(const int32_t* ids, int R, int E,
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = lane_id();
+  const int len = r1 - r0;
 
-  const int nw = min(NW, max(1, (R + 255) / 256));   // waves that walk pairs
+  const int nw = min(NW, max(1, (len + 255) / 256));   // waves that walk pairs
   for (int i = tid; i < nw * E; i += NT) hist[i] = 0;
   __syncthreads();
 
-  const int per = (R + nw - 1) / nw;
-  const int beg = wave < nw ? min(R, wave * per) : R;
-  const int end = wave < nw ? min(R, beg + per) : R;
+  const int per = (len + nw - 1) / nw;
+  const int beg = r0 + (wave < nw ? min(len, wave * per) : len);
+  const int end = wave < nw ? min(r1, beg + per) : r1;
   const bool kept = end - beg <= kBatch * kWave;     // the range fits one batch
   int32_t* my_hist = hist + wave * E;
   int raw[kBatch];
@@ -167,16 +173,17 @@ __device__ __forceinline__ void permute_block(const int32_t* ids, int R, int E,
 
   // 2a. exclusive base of each wave within each expert; totals
   for (int e = tid; e < E; e += NT) {
-    int run = 0;
+    int run = gbase ? gbase[e] : 0;
     for (int w = 0; w < nw; ++w) {
       const int c = hist[w * E + e];
       hist[w * E + e] = run;
       run += c;
     }
     tot[e] = run;
-    counts[e] = run;
+    if (!gbase) counts[e] = run;
   }
   __syncthreads();
+  if (!gbase) {
 
   // 2b. exclusive scan of the totals over experts (each thread: ept experts)
   const int ept = (E + NT - 1) / NT;
@@ -202,6 +209,7 @@ __device__ __forceinline__ void permute_block(const int32_t* ids, int R, int E,
     offsets[E] = total;                       // == R when every id is in range
   }
   __syncthreads();
+  }
 
   // 3. stable scatter; my_hist[e] is the next free row of expert e for this wave
   const int nbits = (E > 1) ? 32 - __clz(E - 1) : 0;

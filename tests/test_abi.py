@@ -80,6 +80,13 @@ def test_route_permute_argument_checks(lib):
                                  None) == 0
     assert lib.moe_route_topk(None, 0, 8, 2, None, None, None) == 0
     assert lib.moe_permute_workspace_bytes(64, 384, 8) == 0
+    # above 8192 pairs: one E-int histogram per range of 1024 pairs
+    assert lib.moe_permute_workspace_bytes(1024, 384, 8) == 0
+    assert lib.moe_permute_workspace_bytes(1025, 384, 8) == 9 * 384 * 4
+    assert lib.moe_permute_workspace_bytes(8192, 384, 8) == 64 * 384 * 4
+    assert lib.moe_permute_workspace_bytes(8192, 2000, 8) == 0          # E > 1024: invalid
+    # a needed workspace may not be NULL
+    assert lib.moe_permute(P, 8192, 384, 8, P, P, P, P, None, 64 * 384 * 4, None) == -1
     assert lib.moe_permute(P, 4, 8, 2, P, P, P, None, None, 0, None) == -1
     assert lib.moe_permute(P, 4, 8, 9, P, P, P, P, None, 0, None) == -2
 
