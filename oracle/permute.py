@@ -12,12 +12,18 @@ computation needs once routing is known.  Definition used:
   pair_to_row    inverse: sorted_pairs[pair_to_row[p]] == p.
 
 Built by walking the pairs in order and appending each to its expert's list.
+
+With drop_invalid=True (the library's rule for bad input, a reading: the
+pages never route outside the experts) a pair whose id is outside [0, E) is
+left out: it is not counted, has no row (pair_to_row = -1) and offsets[E]
+counts only the kept pairs; sorted_pairs holds offsets[E] entries followed
+by -1.
 """
 
 import numpy as np
 
 
-def permute(ids, E):
+def permute(ids, E, drop_invalid=False):
     """ids int[T, k] -> dict(counts, offsets, sorted_pairs, pair_to_row), all int32."""
     ids = np.asarray(ids)
     if ids.ndim != 2:
@@ -29,6 +35,8 @@ def permute(ids, E):
     for p in range(R):
         e = flat[p]
         if not 0 <= e < E:
+            if drop_invalid:
+                continue
             raise ValueError("expert id out of range")
         lists[e].append(p)
     counts = np.array([len(lst) for lst in lists], dtype=np.int32)
@@ -38,8 +46,8 @@ def permute(ids, E):
         offsets[e] = running
         running += len(lists[e])
     offsets[E] = running
-    sorted_pairs = np.zeros(R, dtype=np.int32)
-    pair_to_row = np.zeros(R, dtype=np.int32)
+    sorted_pairs = np.full(R, -1, dtype=np.int32)
+    pair_to_row = np.full(R, -1, dtype=np.int32)
     row = 0
     for e in range(E):
         for p in lists[e]:

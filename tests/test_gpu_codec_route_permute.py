@@ -192,6 +192,23 @@ def test_permute_edge_shapes(mm, T, E, k, mode):
     check_permute(mm, ids, E)
 
 
+@pytest.mark.parametrize("T,E,k", [(60, 384, 8), (4000, 384, 8), (1200, 1024, 32)])
+def test_permute_drops_out_of_range_ids(mm, T, E, k):
+    """Ids outside [0, E) are dropped (one workgroup up to 8192 pairs, ranges
+    above): the kept pairs' lists as the oracle's drop mode gives them."""
+    rng = np.random.default_rng(T + E + k)
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)])
+    bad = rng.random(ids.shape) < 0.05
+    ids = np.where(bad, rng.choice([-1, E, E + 3, -7], size=ids.shape), ids).astype(np.int32)
+    got = mm.moe_permute(torch.from_numpy(ids).to(DEV), E)
+    torch.cuda.synchronize()
+    ref = operm.permute(ids, E, drop_invalid=True)
+    kept = int(ref["offsets"][E])
+    for name, g in zip(("counts", "offsets", "pair_to_row"), (got[0], got[1], got[3])):
+        assert np.array_equal(g.cpu().numpy(), ref[name]), name
+    assert np.array_equal(got[2].cpu().numpy()[:kept], ref["sorted_pairs"][:kept])
+
+
 # ---------------------------------------------------------------------------
 # routing and grouping in one call (one fused workgroup up to 16 tokens)
 

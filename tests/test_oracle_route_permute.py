@@ -117,6 +117,31 @@ def test_permute_rejects_out_of_range():
         operm.permute(np.array([[0, 5]]), 4)
 
 
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_permute_drop_invalid_equals_an_extra_expert_removed(seed):
+    """Dropping the pairs with ids outside [0, E) gives what routing them to
+    an extra expert E gives, with that last segment cut off; on valid input
+    the drop mode changes nothing."""
+    rng = np.random.default_rng(seed)
+    T, E, k = 300, 48, 6
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)])
+    assert all(np.array_equal(operm.permute(ids, E, drop_invalid=True)[n], v)
+               for n, v in operm.permute(ids, E).items())
+    bad = rng.random(ids.shape) < 0.07
+    ids_bad = np.where(bad, rng.choice([-1, E, E + 7, -100], size=ids.shape), ids)
+    d = operm.permute(ids_bad, E, drop_invalid=True)
+    ref = operm.permute(np.where(bad, E, ids), E + 1)          # the bad pairs as expert E
+    kept = ref["offsets"][E]
+    assert np.array_equal(d["counts"], ref["counts"][:E])
+    assert np.array_equal(d["offsets"], ref["offsets"][:E + 1])
+    assert d["offsets"][E] == (~bad).sum()
+    assert np.array_equal(d["sorted_pairs"][:kept], ref["sorted_pairs"][:kept])
+    assert np.all(d["sorted_pairs"][kept:] == -1)
+    flat_bad = bad.reshape(-1)
+    assert np.all(d["pair_to_row"][flat_bad] == -1)
+    assert np.array_equal(d["pair_to_row"][~flat_bad], ref["pair_to_row"][~flat_bad])
+
+
 # ---- router projection (the step in front of the routing)
 
 def _bf16_bits(v):
