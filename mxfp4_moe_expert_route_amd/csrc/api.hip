@@ -50,6 +50,37 @@ bool use_dense(int T, int H, int I, int E, int k) {
 
 }  // namespace
 
+namespace mxm {
+
+int device_cus() {
+  static std::atomic<int> cus[kMaxDevices];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+  const bool cache = dev >= 0 && dev < kMaxDevices;
+  if (cache) {
+    const int n = cus[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+  }
+  int v = 0;
+  if (dev < 0 || hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      v < 1)
+    v = 256;
+  if (cache) cus[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
+hipError_t lds_limit_once(const void* fn, int bytes, std::atomic<bool>* done) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+  const bool cache = dev >= 0 && dev < kMaxDevices;
+  if (cache && done[dev].load(std::memory_order_acquire)) return hipSuccess;
+  const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && cache) done[dev].store(true, std::memory_order_release);
+  return e;
+}
+
+}  // namespace mxm
+
 extern "C" {
 
 int mxm_version(void) { return 100; }

@@ -1,6 +1,7 @@
 // Shared device helpers and the internal launcher interface of libmxfp4moe.
 // gfx950 (CDNA4) only: wave64, MFMA, scaled FP4 conversions.
 #pragma once
+#include <atomic>
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -104,6 +105,16 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, i
   }
   return false;
 }
+
+// ---------------------------------------------------------------------------
+// per-device launch state, kept for the life of the process (atomics: calls
+// may come from several host threads)
+constexpr int kMaxDevices = 64;
+// CU count of the current device (256 when it cannot be read)
+int device_cus();
+// Raise fn's dynamic LDS limit to `bytes` on the current device, once per
+// device: done[] holds one flag per device index.
+hipError_t lds_limit_once(const void* fn, int bytes, std::atomic<bool>* done);
 
 // ---------------------------------------------------------------------------
 // internal launchers (defined in the kernel files, called by api.hip after

@@ -421,24 +421,12 @@ __global__ __launch_bounds__(kThreadsDec) void k_decode(
   }
 }
 
-int cu_count() {
-  static int n = 0;
-  if (n == 0) {
-    int dev = 0, v = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v < 1)
-      v = 256;
-    n = v;
-  }
-  return n;
-}
-
 // Upper bound of the units a workgroup can get (the host does not know the
 // counts; tiles <= min(E, R) + R / 16).
 int64_t max_units_per_wg(int R, int E, int ntile_n) {
   const int64_t tiles = int64_t(R < E ? R : E) + R / kTokRows;
   const int64_t U = tiles * ntile_n;
-  const int G = cu_count();
+  const int G = device_cus();
   return (U + G - 1) / G + 1;
 }
 
@@ -446,16 +434,13 @@ template <bool GU>
 hipError_t launch_decode(const uint16_t* act, const int32_t* sp, const int32_t* off, int H, int I,
                          int E, int k, const uint8_t* c, const uint8_t* sc, void* out, int hi,
                          hipStream_t s) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_decode<GU>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, kLdsDec);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<bool> lds_set[kMaxDevices];
+  const hipError_t e =
+      lds_limit_once(reinterpret_cast<const void*>(&k_decode<GU>), kLdsDec, lds_set);
+  if (e != hipSuccess) return e;
   const int K = GU ? H : I;
   const int ntile_n = GU ? I / 128 : H / kUnitRows;
-  k_decode<GU><<<dim3(unsigned(cu_count())), kThreadsDec, kLdsDec, s>>>(
+  k_decode<GU><<<dim3(unsigned(device_cus())), kThreadsDec, kLdsDec, s>>>(
       act, sp, off, K, I, H, E, k, c, sc, out, ntile_n, hi);
   return hipGetLastError();
 }

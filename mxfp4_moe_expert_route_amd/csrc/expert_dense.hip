@@ -492,31 +492,16 @@ __global__ __launch_bounds__(kDThreads, 1) void k_dense(
   }
 }
 
-int cu_count() {
-  static int n = 0;
-  if (n == 0) {
-    int dev = 0, v = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v < 1)
-      v = 256;
-    n = v;
-  }
-  return n;
-}
-
 template <bool GU>
 hipError_t launch_dense(const uint16_t* act, uint32_t act_bytes, const int32_t* sorted_pairs,
                         const int32_t* offsets, int H, int I, int E, int k, const uint8_t* codes,
                         const uint8_t* scales, void* out, hipStream_t s) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_dense<GU>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<bool> lds_set[kMaxDevices];
+  const hipError_t e =
+      lds_limit_once(reinterpret_cast<const void*>(&k_dense<GU>), kLdsBytes, lds_set);
+  if (e != hipSuccess) return e;
   const int K = GU ? H : I;
-  const int grid = (cu_count() + 7) / 8 * 8;      // one per CU, a multiple of 8
+  const int grid = (device_cus() + 7) / 8 * 8;      // one per CU, a multiple of 8
   k_dense<GU><<<dim3(unsigned(grid)), kDThreads, kLdsBytes, s>>>(
       act, act_bytes, sorted_pairs, offsets, K, I, H, E, k, codes, scales, out, kMinRows);
   return hipGetLastError();

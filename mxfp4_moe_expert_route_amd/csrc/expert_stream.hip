@@ -316,21 +316,9 @@ int choose_ms(int R, int E) {
 
 int tile_slots(int R, int E, int mt) { return (R < E ? R : E) + (R + mt - 1) / mt; }
 
-int stream_cus() {
-  static int n = 0;
-  if (n == 0) {
-    int dev = 0, v = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v < 1)
-      v = 256;
-    n = v;
-  }
-  return n;
-}
-
 // workgroups launched: the tile-slot bound, capped at a few per CU
 unsigned stream_grid(int64_t slots_times_n) {
-  const int64_t cap = int64_t(4) * stream_cus();
+  const int64_t cap = int64_t(4) * device_cus();
   return unsigned(slots_times_n < cap ? slots_times_n : cap);
 }
 

@@ -125,14 +125,10 @@ hipError_t launch_permute(const int32_t* ids, int T, int E, int k, int32_t* coun
         ids, R, E, counts, offsets, sorted_pairs, pair_to_row);
     return hipGetLastError();
   }
-  static bool attr_set = false;
-  if (!attr_set) {                // 17 E ints, E up to 1024: more than the default 64 KB
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_permute<16>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             int(17 * 1024 * sizeof(int32_t)));
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<bool> lds_set[kMaxDevices];   // 17 E ints, E up to 1024: above 64 KB
+  const hipError_t e = lds_limit_once(reinterpret_cast<const void*>(&k_permute<16>),
+                                      int(17 * 1024 * sizeof(int32_t)), lds_set);
+  if (e != hipSuccess) return e;
   k_permute<16><<<1, 16 * kWave, size_t(17) * E * sizeof(int32_t), s>>>(
       ids, R, E, counts, offsets, sorted_pairs, pair_to_row);
   return hipGetLastError();
