@@ -53,7 +53,10 @@ __global__ __launch_bounds__(256) void k_perm_hist(const int32_t* __restrict__ i
   for (int e = threadIdx.x; e < E; e += 256) ws[size_t(blockIdx.x) * E + e] = hist[e];
 }
 
-// one thread per expert (E <= 1024)
+// one thread per expert (E <= 1024); a thread's counts over the ranges are
+// read 16 at a time, all loads of a batch in flight together
+constexpr int kScanBatch = 16;
+
 __global__ __launch_bounds__(1024) void k_perm_scan(int E, int nr, int32_t* __restrict__ ws,
                                                     int32_t* __restrict__ counts,
                                                     int32_t* __restrict__ offsets) {
@@ -61,7 +64,13 @@ __global__ __launch_bounds__(1024) void k_perm_scan(int E, int nr, int32_t* __re
   const int e = threadIdx.x, lane = lane_id(), wave = e / kWave;
   int total = 0;
   if (e < E)
-    for (int b = 0; b < nr; ++b) total += ws[size_t(b) * E + e];
+    for (int b0 = 0; b0 < nr; b0 += kScanBatch) {
+      int v[kScanBatch];
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i) v[i] = b0 + i < nr ? ws[size_t(b0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i) total += v[i];
+    }
   const int incl = wave_incl_scan(total);
   if (lane == kWave - 1) wave_tot[wave] = incl;
   __syncthreads();
@@ -73,10 +82,15 @@ __global__ __launch_bounds__(1024) void k_perm_scan(int E, int nr, int32_t* __re
   if (e < E) {
     counts[e] = total;
     offsets[e] = run;
-    for (int b = 0; b < nr; ++b) {
-      const int c = ws[size_t(b) * E + e];
-      ws[size_t(b) * E + e] = run;
-      run += c;
+    for (int b0 = 0; b0 < nr; b0 += kScanBatch) {
+      int v[kScanBatch];
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i) v[i] = b0 + i < nr ? ws[size_t(b0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i) {
+        if (b0 + i < nr) ws[size_t(b0 + i) * E + e] = run;
+        run += v[i];
+      }
     }
   }
   if (e == 0) offsets[E] = all;
