@@ -11,8 +11,11 @@
 // Items are ordered expert by expert, n-tile by n-tile, m-tile fastest, and
 // the list is cut into eight equal contiguous ranges, one per XCD (workgroup
 // b runs on XCD b % 8).  The workgroups of an XCD (one per CU) take its items
-// round-robin, so at any time they work on neighbouring items: the n-tiles of
-// one m-tile read the same activation rows from that XCD's L2.  An m-tile
+// in rounds, one item each, in ascending order in even rounds and descending
+// in odd ones (an expert's small last m-tile sits beside a full one, so a
+// fixed order would hand the cheap items to the same workgroups round after
+// round).  At any time they work on neighbouring items: the n-tiles of one
+// m-tile read the same activation rows from that XCD's L2.  An m-tile
 // covers every row of a typical expert, so each weight byte leaves HBM once.
 //
 // The loads are sized by cache lines, the currency of the CU's load path:
@@ -472,7 +475,14 @@ __global__ __launch_bounds__(kDThreads, 1) void k_dense(
   const __amdgpu_buffer_rsrc_t rs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(act), 0, int(act_bytes), 0x00020000);
 
-  for (int v = v0 + int(blockIdx.x >> 3); v < v1; v += gx) {
+  // round r of the XCD's items goes to its workgroups in ascending order when
+  // r is even and descending when odd, so cheap and dear neighbours (the
+  // small last m-tile of an expert beside a full one) even out over rounds
+  const int wi = int(blockIdx.x >> 3);
+  for (int r = 0;; ++r) {
+    const int v = v0 + r * gx + ((r & 1) ? gx - 1 - wi : wi);
+    if (v0 + r * gx >= v1) break;
+    if (v >= v1) continue;
     const int tau = v / ntn;
     const int e = expert_of(mpre, E, tau);
     const int mt = mpre[e + 1] - mpre[e];
