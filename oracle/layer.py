@@ -9,7 +9,7 @@ Summary").  The backbone verifies a block of 8 drafted tokens per sequence in
 one step (§3, mask block capped at 8), so a decode step runs this layer on
 8 tokens per sequence.
 
-Readings (listed in the design doc), where the pages are silent:
+Readings, where the pages are silent:
   * each expert is a SwiGLU FFN without biases: g = W_gate x, u = W_up x,
     h = silu(g) * u with silu(g) = g / (1 + exp(-g)), y = W_down h;
   * the stacked gate/up matrix W13 [2I, H] holds gate rows 0..I-1 then up
@@ -36,13 +36,19 @@ def silu(g):
     return g / (1.0 + np.exp(-g))
 
 
+def gate_up_swiglu(x64, w13_codes, w13_scales):
+    """Rows x64 float64[n, H] against 2C weight rows (C gate rows, then the up
+    rows of the same C columns) -> h_bits uint16[n, C] = bf16(silu(g) * u)."""
+    W13 = mx.unpack(w13_codes, w13_scales)      # [2C, H]
+    C = W13.shape[0] // 2
+    g = x64 @ W13[:C].T
+    u = x64 @ W13[C:].T
+    return mx.to_bf16_bits(silu(g) * u)
+
+
 def expert_ffn(x64, w13_codes, w13_scales, w2_codes, w2_scales):
     """One expert on rows x64 float64[n, H] -> (h_bits uint16[n, I], y float32[n, H])."""
-    W13 = mx.unpack(w13_codes, w13_scales)      # [2I, H]
-    I = W13.shape[0] // 2
-    g = x64 @ W13[:I].T
-    u = x64 @ W13[I:].T
-    h_bits = mx.to_bf16_bits(silu(g) * u)
+    h_bits = gate_up_swiglu(x64, w13_codes, w13_scales)
     h = mx.bf16_bits_to_f64(h_bits)
     W2 = mx.unpack(w2_codes, w2_scales)         # [H, I]
     y = mx.to_f32(h @ W2.T)

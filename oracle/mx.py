@@ -6,7 +6,7 @@ nxbn.cn article, "量化策略的智能选择": store_dtype mxfp4, mxfp4_block_s
 MXFP4 is the OCP MX v1.0 format: each element is an FP4 E2M1 number and each
 block of 32 consecutive elements shares one E8M0 power-of-two scale.
 
-Readings where the pages are silent (each is also listed in the design doc):
+Readings where the pages are silent:
   * blocks run along the last (reduction, K) axis of each row;
   * byte j of a packed row holds element 2j in bits 3..0 and element 2j+1 in
     bits 7..4;

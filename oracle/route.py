@@ -5,7 +5,7 @@ The pages give the routing shape only: 384 experts with 8 active per token
 card's §4 "Model Summary" gives hidden size 6144 and 1.02T total / 42B active
 parameters) and call the routing dynamic ("动态路由", same article,
 "内存优化技巧").  The scoring rule is not on the pages; the reading used
-here, listed in DESIGN.md, is:
+here is:
 
   * the input is fp32 router logits [T, E] (the router projection itself is
     upstream of this layer);

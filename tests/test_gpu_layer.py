@@ -157,3 +157,68 @@ def test_layer_page_shaped_sampled(mm, name, n):
     b, ref, _ = check_layer(cfg, x, logits, whost, wdev, tokens=tok)
     touched = int((b.counts.cpu().numpy() > 0).sum())
     say("  %s: touched experts %d" % (name, touched))
+
+
+@pytest.mark.parametrize("name", ["verify_t64", "zipf_t512", "prefill_t8192"])
+def test_page_shaped_every_block_written_and_sampled(mm, name):
+    """At full size, in the benchmark's launch configuration: every element of
+    h, y and the output is written (the buffers start as NaN), and h is checked
+    against the oracle at one (row, column) of every block of 192 rows of an
+    expert x 128 columns: each work item of the contraction kernels (a tile of
+    at most 192 rows by 128 gate columns with their up columns) gets one
+    sampled element, so a skipped, repeated or misplaced item shows."""
+    from oracle import layer as olayer, mx as omx
+    from oracle import permute as operm, route as oroute
+    from _gpu import dev_bf16, bf16_ulp_diff
+    cfg = workloads.CONFIGS[name]
+    whost, wdev = page_layer_weights()
+    x_bits = workloads.gen_x_bits(cfg, 0)
+    logits = workloads.gen_logits(cfg, x_bits, 0)
+    T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
+    x = dev_bf16(x_bits)
+    lg = torch.from_numpy(logits).to("cuda")
+    ids_d, w_d, counts_d, offs_d, sp_d, p2r_d = mm.moe_route_permute(lg, k)
+    h = torch.full((T * k, I), float("nan"), dtype=torch.bfloat16, device="cuda")
+    y = torch.full((T * k, H), float("nan"), dtype=torch.float32, device="cuda")
+    out = torch.full((T, H), float("nan"), dtype=torch.float32, device="cuda")
+    mm.moe_mxfp4_gate_up_swiglu(x, sp_d, offs_d, k, wdev["w13_codes"], wdev["w13_scales"], h=h)
+    mm.moe_mxfp4_down(h, offs_d, k, wdev["w2_codes"], wdev["w2_scales"], y=y)
+    mm.moe_combine(y, w_d, p2r_d, out=out)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(h).all()), "h has unwritten (NaN) elements"
+    assert bool(torch.isfinite(y).all()), "y has unwritten (NaN) elements"
+    assert bool(torch.isfinite(out).all()), "out has unwritten (NaN) elements"
+
+    ids, _ = oroute.route_topk(logits, k)
+    lists = operm.permute(ids, E)
+    assert np.array_equal(offs_d.cpu().numpy(), lists["offsets"])
+    offsets, sorted_pairs = lists["offsets"], lists["sorted_pairs"]
+    rng = np.random.default_rng(7)
+    rows, cols = [], []
+    for e in range(E):
+        n_e = int(offsets[e + 1] - offsets[e])
+        for r0 in range(0, n_e, 192):
+            nr = min(192, n_e - r0)
+            for c0 in range(0, I, 128):
+                rows.append(int(offsets[e]) + r0 + int(rng.integers(nr)))
+                cols.append(c0 + int(rng.integers(128)))
+    rows, cols = np.array(rows), np.array(cols)
+    hg_bits = h.view(torch.int16).cpu().numpy().view(np.uint16)[rows, cols]
+    experts = np.searchsorted(offsets, rows, side="right") - 1
+    tokens = sorted_pairs[rows] // k
+    X = omx.bf16_bits_to_f64(x_bits[tokens])
+    hr_bits = np.empty(len(rows), np.uint16)
+    for i in range(len(rows)):
+        e, c = experts[i], cols[i]
+        sel = [c, I + c]
+        hr_bits[i] = olayer.gate_up_swiglu(X[i:i + 1], whost["w13_codes"][e][sel],
+                                           whost["w13_scales"][e][sel])[0, 0]
+    d = bf16_ulp_diff(hg_bits, hr_bits)
+    hg, hr = omx.bf16_bits_to_f64(hg_bits), omx.bf16_bits_to_f64(hr_bits)
+    rms = np.sqrt(np.mean(hr ** 2))
+    _, ex = np.frexp(np.where(hr != 0, np.abs(hr), 1.0))
+    ulp = np.ldexp(1.0, (ex - 1 - 7).astype(np.int32))
+    say("  %s: %d sampled h elements (one per block), %.3f%% differ, max %d ulp"
+        % (name, len(rows), 100.0 * (d > 0).mean(), int(d.max())))
+    assert np.all(np.abs(hg - hr) <= np.maximum(ulp, 1e-2 * rms)), "h element out of bound"
+    assert (d > 1).mean() <= 1e-3
