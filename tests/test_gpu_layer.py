@@ -163,10 +163,12 @@ def test_layer_page_shaped_sampled(mm, name, n):
 def test_page_shaped_every_block_written_and_sampled(mm, name):
     """At full size, in the benchmark's launch configuration: every element of
     h, y and the output is written (the buffers start as NaN), and h is checked
-    against the oracle at one (row, column) of every block of 192 rows of an
-    expert x 128 columns: each work item of the contraction kernels (a tile of
-    at most 192 rows by 128 gate columns with their up columns) gets one
-    sampled element, so a skipped, repeated or misplaced item shows."""
+    against the oracle at one (row, column) of every block of an expert's rows
+    x 128 columns, the blocks 192 rows long for experts with at least 64 rows
+    and 16 rows long for the others.  These are the work items of the
+    contraction kernels (192 or 16 token rows by 128 gate columns with their up
+    columns), so each item gets one sampled element and a skipped, repeated or
+    misplaced item shows."""
     from oracle import layer as olayer, mx as omx
     from oracle import permute as operm, route as oroute
     from _gpu import dev_bf16, bf16_ulp_diff
@@ -197,8 +199,9 @@ def test_page_shaped_every_block_written_and_sampled(mm, name):
     rows, cols = [], []
     for e in range(E):
         n_e = int(offsets[e + 1] - offsets[e])
-        for r0 in range(0, n_e, 192):
-            nr = min(192, n_e - r0)
+        blk = 192 if n_e >= 64 else 16
+        for r0 in range(0, n_e, blk):
+            nr = min(blk, n_e - r0)
             for c0 in range(0, I, 128):
                 rows.append(int(offsets[e]) + r0 + int(rng.integers(nr)))
                 cols.append(c0 + int(rng.integers(128)))
