@@ -21,7 +21,8 @@
  * Conventions for every call
  *   - All array arguments are DEVICE pointers, allocated and owned by the
  *     caller.  The library never allocates or frees device memory and keeps
- *     no state between calls; calls are thread-safe.
+ *     no data between calls (it caches, per device, only the CU count and
+ *     whether a kernel's LDS limit has been raised); calls are thread-safe.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Each call only enqueues kernels on it and returns; there is no host
  *     synchronisation.  Results are valid once the stream reaches them.
