@@ -11,8 +11,10 @@ namespace {
 
 // One workgroup per (token, 2048 columns): the token's k rows and weights are
 // read once into LDS, then every thread issues its 2k row loads together (two
-// float4 per row, 1024 columns apart; no branch between them: a dropped pair
-// reads row 0 and its term is not added) and accumulates them in slot order.
+// 16-byte loads per row, 1024 columns apart; no branch between them: a
+// dropped pair reads row 0 and its term is not added) and accumulates them in
+// slot order.  Each row of y is read once, so the loads carry the
+// non-temporal hint (at 8192 tokens x top-8: 380 -> 318 us).
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y,
                                                  const float* __restrict__ w,
                                                  const int32_t* __restrict__ pair_to_row, int T,
@@ -30,23 +32,24 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y,
   if (c0 >= H) return;
   float4 acc0 = make_float4(0.f, 0.f, 0.f, 0.f), acc1 = acc0;
   for (int j0 = 0; j0 < k; j0 += 8) {
-    float4 v0[8], v1[8];
+    f32x4 v0[8], v1[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int r = (j0 + i < k) ? max(srow[j0 + i], 0) : 0;
       const float* yr = y + int64_t(r) * H + c0;
-      v0[i] = *reinterpret_cast<const float4*>(yr);
-      v1[i] = in1 ? *reinterpret_cast<const float4*>(yr + 1024) : make_float4(0.f, 0.f, 0.f, 0.f);
+      v0[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(yr));
+      v1[i] = in1 ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(yr + 1024))
+                  : f32x4{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int j = j0 + i;
       if (j < k && srow[j] >= 0) {
         const float wj = sw[j];
-        acc0.x = fmaf(wj, v0[i].x, acc0.x); acc0.y = fmaf(wj, v0[i].y, acc0.y);
-        acc0.z = fmaf(wj, v0[i].z, acc0.z); acc0.w = fmaf(wj, v0[i].w, acc0.w);
-        acc1.x = fmaf(wj, v1[i].x, acc1.x); acc1.y = fmaf(wj, v1[i].y, acc1.y);
-        acc1.z = fmaf(wj, v1[i].z, acc1.z); acc1.w = fmaf(wj, v1[i].w, acc1.w);
+        acc0.x = fmaf(wj, v0[i][0], acc0.x); acc0.y = fmaf(wj, v0[i][1], acc0.y);
+        acc0.z = fmaf(wj, v0[i][2], acc0.z); acc0.w = fmaf(wj, v0[i][3], acc0.w);
+        acc1.x = fmaf(wj, v1[i][0], acc1.x); acc1.y = fmaf(wj, v1[i][1], acc1.y);
+        acc1.z = fmaf(wj, v1[i][2], acc1.z); acc1.w = fmaf(wj, v1[i][3], acc1.w);
       }
     }
   }
