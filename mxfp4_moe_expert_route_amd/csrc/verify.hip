@@ -95,7 +95,15 @@ __global__ __launch_bounds__(kVT) void k_verify_stats(const float* __restrict__ 
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
       const int c = cb + j * kVT + tid;
-      v[j] = c < nc ? src[c] : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+      // the rows stream through once here (only row n of each block is read
+      // again, in the next step): non-temporal loads, 90 -> 85 us at 64
+      // blocks
+      if (c < nc) {
+        const f32x4 t = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + c));
+        v[j] = make_float4(t[0], t[1], t[2], t[3]);
+      } else {
+        v[j] = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+      }
     }
     float bm = -INFINITY;
 #pragma unroll
