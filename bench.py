@@ -33,6 +33,7 @@ METRIC = "MXFP4 MoE layer tokens/s + effective weight GB/s (% HBM peak) on 1 MI3
 HBM_PEAK_GBPS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 FP32_VALU_PEAK_TFLOPS = 157.3
+LLC_BYTES = 256 * 1024 * 1024                 # MI355X last-level (Infinity) cache
 
 
 def log(*a):
@@ -214,20 +215,24 @@ def bench_router(args, cfg, torch, mm, workloads):
     warmup = args.warmup if args.warmup is not None else 20
     T, H, E, k = cfg.T, cfg.H, cfg.E, cfg.k
     x = torch.from_numpy(workloads.gen_x_bits(cfg, 0).view(np.int16)).view(torch.bfloat16).to(dev)
-    w = [torch.from_numpy(workloads.gen_router(cfg, 0)).to(dev) for _ in range(2)]
+    # enough copies of the router weights that together they are twice the
+    # 256 MB last-level cache, used in turn, so each call reads its copy from HBM
+    w0 = torch.from_numpy(workloads.gen_router(cfg, 0)).to(dev)
+    ncopy = max(2, -(-2 * LLC_BYTES // (E * H * 4)))
+    w = [w0] + [w0.clone() for _ in range(ncopy - 1)]
     bias = torch.from_numpy(workloads.gen_bias(cfg, 0).astype(np.float32)).to(dev)
     logits = torch.empty(T, E, dtype=torch.float32, device=dev)
     ids = torch.empty(T, k, dtype=torch.int32, device=dev)
     tw = torch.empty(T, k, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
     for i in range(warmup):
-        mm.moe_router_topk(x, w[i & 1], k, bias, logits, ids, tw)
+        mm.moe_router_topk(x, w[i % ncopy], k, bias, logits, ids, tw)
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for i in range(steps):
-        mm.moe_router_topk(x, w[i & 1], k, bias, logits, ids, tw)
+        mm.moe_router_topk(x, w[i % ncopy], k, bias, logits, ids, tw)
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
@@ -269,20 +274,25 @@ def bench_verify(args, cfg, torch, mm, workloads):
         print("bench.py: --verify runs workloads of up to 512 tokens (64 blocks)", file=sys.stderr)
         sys.exit(2)
     tg, dr, tk, u = workloads.gen_verify_inputs(B, L, V, 0)
-    ins = [tuple(torch.from_numpy(a).to(dev) for a in (tg, dr, tk, u)) for _ in range(2)]
+    # enough copies of the inputs that together they are twice the last-level
+    # cache, used in turn, so each call reads its inputs from HBM
+    in0 = tuple(torch.from_numpy(a).to(dev) for a in (tg, dr, tk, u))
+    set_bytes = sum(a.numel() * a.element_size() for a in in0)
+    ncopy = max(2, -(-2 * LLC_BYTES // set_bytes))
+    ins = [in0] + [tuple(a.clone() for a in in0) for _ in range(ncopy - 1)]
     n = torch.empty(B, dtype=torch.int32, device=dev)
     t = torch.empty(B, dtype=torch.int32, device=dev)
     ws = torch.empty(max(8, int(mm._lib.lib().dflash_verify_workspace_bytes(B, L, V))),
                      dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     for i in range(warmup):
-        mm.dflash_verify_accept(*ins[i & 1], n, t, ws)
+        mm.dflash_verify_accept(*ins[i % ncopy], n, t, ws)
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for i in range(steps):
-        mm.dflash_verify_accept(*ins[i & 1], n, t, ws)
+        mm.dflash_verify_accept(*ins[i % ncopy], n, t, ws)
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps

@@ -105,7 +105,17 @@ __global__ __launch_bounds__(256) void k_router_rows(const uint16_t* __restrict_
     float4 w[EPW];
 #pragma unroll
     for (int q = 0; q < EPW; ++q)
-      w[q] = *reinterpret_cast<const float4*>(wr + size_t(e0 + min(q, ne - 1)) * H + h);
+    {
+      // one token block reads each weight row once: non-temporal (8 tokens:
+      // 20.3 -> 19.4 us); several blocks re-read the rows from the caches
+      const float* wp = wr + size_t(e0 + min(q, ne - 1)) * H + h;
+      if (gridDim.y == 1) {
+        const f32x4 t = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(wp));
+        w[q] = make_float4(t[0], t[1], t[2], t[3]);
+      } else {
+        w[q] = *reinterpret_cast<const float4*>(wp);
+      }
+    }
 #pragma unroll
     for (int j = 0; j < TB; ++j) {
       if (j < nt) {
