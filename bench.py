@@ -1,19 +1,27 @@
 """Benchmark of the MXFP4 MoE expert layer on one MI355X.
 
 One step = the whole layer (moe_route_permute (top-k routing and grouping by
-expert) -> moe_mxfp4_gate_up_swiglu -> moe_mxfp4_down -> moe_combine) over one batch of
-synthetic tokens, inputs resident in HBM.  Default workload: the page-shaped
-layer (hidden 6144, 384 experts, top-8, intermediate 2048, MXFP4 block 32)
-verifying one sequence's 8-token draft block.  Two copies of the expert
-weights alternate between steps so the 256 MB last-level cache cannot serve
-them.
+expert) -> moe_mxfp4_gate_up_swiglu -> moe_mxfp4_down -> moe_combine) over one
+batch of synthetic tokens, inputs resident in HBM.  Default workload: the
+page-shaped layer (hidden 6144, 384 experts, top-8, intermediate 2048, MXFP4
+block 32) verifying one sequence's 8-token draft block.  Two copies of the
+expert weights alternate between steps so the 256 MB last-level cache cannot
+serve them.
+
+Each workload runs --warmup steps, then more until --warm-seconds have passed
+(the clocks settle under sustained load), then three timed passes of --steps
+steps: the headline region (two events around all steps), per-step events
+(median / p10 / p90) and events around every entry point (per-kernel times).
+The verify_t8 run then times verify_t64, zipf_t512 and prefill_t8192 on the
+same weights with the same flags.
 
 Prints ONE JSON line on stdout; diagnostics go to stderr.
-  value       tokens/s of the whole layer
-  roofline    the gate/up contraction (the kernel that streams 2/3 of the
-              weight bytes): algorithmic bytes per launch / its mean duration
-              from HIP events recorded around it on its stream inside the
-              timed region, against 8 TB/s
+  value         tokens/s of the whole layer (headline region)
+  roofline      the gate/up contraction (the kernel that streams 2/3 of the
+                weight bytes): algorithmic bytes per launch / its mean duration
+                from HIP events around its calls, against 8 TB/s (or the bf16
+                MFMA peak where it is compute-bound)
+  workloads     the same figures for the other page-shaped workloads
   cpu_baseline  the float64 CPU oracle on a bounded sample of the same tokens
 """
 
@@ -28,6 +36,8 @@ import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402  (seeded input generators; no layer arithmetic)
 
 METRIC = "MXFP4 MoE layer tokens/s + effective weight GB/s (% HBM peak) on 1 MI355X"
 HBM_PEAK_GBPS = 8000.0
@@ -130,6 +140,45 @@ def _algorithmic_bytes(cfg, counts):
             "moe_mxfp4_down": touched * w2, "touched": touched}
 
 
+def _short_kernel_name(n):
+    return n.replace("mxm::(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+
+
+def _is_phase_marker(name):
+    # torch.cuda._sleep, launched by time_layer at the start of each workload
+    return "spin_kernel" in name or "sleep" in name.lower()
+
+
+def trace_tables(trace_dir, phases):
+    """Per-workload kernel statistics from a rocprofv3 kernel trace of one
+    bench.py run: the dispatches are cut at the marker kernel that starts
+    each workload, in the order `phases` names them."""
+    rows = _csv_rows(_find_csv(trace_dir, "kernel_trace.csv"))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    seg, per = -1, {}
+    for r in rows:
+        name = r["Kernel_Name"]
+        if _is_phase_marker(name):
+            seg += 1
+            continue
+        if seg < 0 or seg >= len(phases):
+            continue
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        per.setdefault(phases[seg], {}).setdefault(_short_kernel_name(name), []).append(dur)
+    out = []
+    for ph in phases:
+        ks = per.get(ph, {})
+        tot = sum(sum(v) for v in ks.values()) or 1.0
+        out += ["Workload %s (every dispatch of the workload: warm-up and timed passes):" % ph, "",
+                "| kernel | calls | average (us) | median (us) | min (us) | max (us) | share |",
+                "|---|---|---|---|---|---|---|"]
+        for n, v in sorted(ks.items(), key=lambda kv: -sum(kv[1])):
+            out.append("| %s | %d | %.1f | %.1f | %.1f | %.1f | %.1f%% |" % (
+                n, len(v), np.mean(v), np.median(v), min(v), max(v), 100.0 * sum(v) / tot))
+        out.append("")
+    return out
+
+
 def summarize_profiles(args):
     """rocprofv3 output of bench.py runs -> the committed summaries.
 
@@ -145,6 +194,8 @@ def summarize_profiles(args):
     if args.command:
         out += ["Command (from /tmp, `TMPDIR=/tmp`, on one MI355X):", "", "```",
                 args.command, "```", ""]
+    if args.trace_dir:
+        out += trace_tables(args.trace_dir, (args.phases or cfg.name).split(","))
     if args.stats_dir:
         rows = _csv_rows(_find_csv(args.stats_dir, "kernel_stats.csv"))
         out += ["| kernel | calls | average (us) | min (us) | max (us) | share |",
@@ -311,25 +362,323 @@ def bench_verify(args, cfg, torch, mm, workloads):
         "cpu_baseline": None}), flush=True)
 
 
+# ---------------------------------------------------------------------------
+# the layer benchmark
+
+# the other page-shaped workloads (same layer weights as verify_t8), timed in
+# the same run after the headline workload
+EXTRA_WORKLOADS = ("verify_t64", "zipf_t512", "prefill_t8192")
+
+
+def host_cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or None
+
+
+class ClockSampler:
+    """Samples the GPU's current shader and memory clock levels from the
+    driver's sysfs files (pp_dpm_sclk / pp_dpm_mclk, the level marked '*')
+    in a host thread while the GPU runs; no GPU call, no child process."""
+
+    def __init__(self, torch):
+        self.paths = {}
+        try:
+            p = torch.cuda.get_device_properties(0)
+            bus = "%04x:%02x:%02x.0" % (getattr(p, "pci_domain_id", 0), p.pci_bus_id,
+                                         p.pci_device_id)
+            base = "/sys/bus/pci/devices/%s" % bus
+            for clk in ("sclk", "mclk", "fclk"):
+                f = "%s/pp_dpm_%s" % (base, clk)
+                if os.path.exists(f):
+                    self.paths[clk] = f
+            self.device = bus
+        except Exception as e:                     # noqa: BLE001 (report, do not fail)
+            self.device = "unknown (%s)" % e
+        self.samples = {c: [] for c in self.paths}
+        self._stop = None
+        self._thread = None
+
+    def _read(self):
+        import re
+        for clk, f in self.paths.items():
+            try:
+                with open(f) as fh:
+                    for line in fh:
+                        if "*" in line:
+                            m = re.search(r"(\d+)\s*[Mm][Hh]z", line)
+                            if m:
+                                self.samples[clk].append(int(m.group(1)))
+            except OSError:
+                pass
+
+    def start(self):
+        import threading
+        if not self.paths:
+            return
+        self._stop = threading.Event()
+
+        def run():
+            while not self._stop.wait(0.02):
+                self._read()
+        self._thread = threading.Thread(target=run, daemon=True)
+        self._thread.start()
+
+    def stop(self):
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join()
+            self._thread = None
+
+    def summary(self):
+        if not self.paths:
+            return {"source": "pp_dpm sysfs files not readable", "device": self.device}
+        out = {"source": "sysfs pp_dpm_* current level, sampled every 20 ms while the "
+                         "layer ran", "device": self.device}
+        for clk, v in self.samples.items():
+            if v:
+                out[clk + "_mhz"] = {"median": int(np.median(v)), "min": int(min(v)),
+                                     "max": int(max(v)), "samples": len(v)}
+        return out
+
+
+def upload_weights(cfg, torch, dev):
+    """Two device copies of all expert weights (steps alternate between them
+    so the 256 MB last-level cache cannot serve the touched experts)."""
+    t0 = time.perf_counter()
+    whost = workloads.all_weights(cfg, 0)
+    log("weights generated in %.1f s (%.2f GB of expert weights)"
+        % (time.perf_counter() - t0, cfg.E * cfg.expert_bytes() / 1e9))
+    names = ("w13_codes", "w13_scales", "w2_codes", "w2_scales")
+    w0 = {k: torch.from_numpy(whost[k]).to(dev) for k in names}
+    w1 = {k: v.clone() for k, v in w0.items()}
+    return whost, (w0, w1)
+
+
+class LayerRun:
+    """One workload's inputs, buffers and step function (the whole layer:
+    routing + grouping, gate/up, down, combine on the current stream)."""
+
+    def __init__(self, cfg, wsets, torch, mm, dev):
+        self.cfg, self.wsets, self.torch, self.mm = cfg, wsets, torch, mm
+        self.x_bits = workloads.gen_x_bits(cfg, 0)
+        self.logits_h = workloads.gen_logits(cfg, self.x_bits, 0)
+        self.x = torch.from_numpy(self.x_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+        self.logits = torch.from_numpy(self.logits_h).to(dev)
+        self.b = mm.LayerBuffers(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, dev)
+        self.stream = torch.cuda.current_stream()
+        self.n = 0                                  # steps run (for the weight copy parity)
+
+    def step(self, ev=None):
+        mm, b, k = self.mm, self.b, self.cfg.k
+        w = self.wsets[self.n & 1]
+        self.n += 1
+        if ev is not None:
+            ev[0].record(self.stream)
+        mm.moe_route_permute(self.logits, k, b.topk_ids, b.topk_w, b.counts, b.offsets,
+                             b.sorted_pairs, b.pair_to_row, b.workspace)
+        if ev is not None:
+            ev[1].record(self.stream)
+        mm.moe_mxfp4_gate_up_swiglu(self.x, b.sorted_pairs, b.offsets, k, w["w13_codes"],
+                                    w["w13_scales"], b.h)
+        if ev is not None:
+            ev[2].record(self.stream)
+        mm.moe_mxfp4_down(b.h, b.offsets, k, w["w2_codes"], w["w2_scales"], b.y)
+        if ev is not None:
+            ev[3].record(self.stream)
+        mm.moe_combine(b.y, b.topk_w, b.pair_to_row, b.out)
+        if ev is not None:
+            ev[4].record(self.stream)
+
+
+def time_layer(run, steps, warmup, warm_s, clocks=None):
+    """Warm up, then three passes of `steps` steps each:
+      1. the headline region: two events around all steps, nothing inside;
+      2. per-step times: one event between consecutive steps;
+      3. per-entry-point times: events around each call of every step.
+    Warm-up is `warmup` steps and then more until `warm_s` seconds have passed
+    (the clocks settle under sustained load)."""
+    torch = run.torch
+    Ev = lambda: torch.cuda.Event(enable_timing=True)       # noqa: E731
+    torch.cuda._sleep(1000)      # marks the start of this workload in a kernel trace
+    for _ in range(warmup):
+        run.step()
+    torch.cuda.synchronize()
+    if clocks is not None:
+        clocks.start()
+    t0 = time.perf_counter()
+    nwarm, batch = warmup, 1
+    while time.perf_counter() - t0 < warm_s:
+        for _ in range(batch):
+            run.step()
+        nwarm += batch
+        torch.cuda.synchronize()
+        batch = min(2 * batch, 512)
+    warm_elapsed = time.perf_counter() - t0
+
+    s = run.stream
+    e0, e1 = Ev(), Ev()
+    wall0 = time.perf_counter()
+    e0.record(s)
+    for _ in range(steps):
+        run.step()
+    e1.record(s)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = e0.elapsed_time(e1) / steps
+
+    evs = [Ev() for _ in range(steps + 1)]
+    evs[0].record(s)
+    for i in range(steps):
+        run.step()
+        evs[i + 1].record(s)
+    torch.cuda.synchronize()
+    per_step = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(steps)])
+
+    kev = [[Ev() for _ in range(5)] for _ in range(steps)]
+    for i in range(steps):
+        run.step(kev[i])
+    torch.cuda.synchronize()
+    if clocks is not None:
+        clocks.stop()
+    parts = ("route_permute", "gate_up", "down", "combine")
+    per_kernel = {p: np.array([kev[i][j].elapsed_time(kev[i][j + 1]) for i in range(steps)])
+                  for j, p in enumerate(parts)}
+    res = {"ms_per_step": ms_step, "wall_ms_per_step": wall * 1e3 / steps,
+           "per_step": per_step, "per_kernel": per_kernel, "warmup_steps": nwarm,
+           "warmup_s": warm_elapsed}
+    log("%s: events %.4f ms/step (wall %.4f), per-step median %.4f p10 %.4f p90 %.4f; "
+        "warm-up %d steps in %.2f s" % (run.cfg.name, ms_step, res["wall_ms_per_step"],
+                                       np.median(per_step), np.percentile(per_step, 10),
+                                       np.percentile(per_step, 90), nwarm, warm_elapsed))
+    log("  " + ", ".join("%s %.1f us" % (p, np.median(v) * 1e3) for p, v in per_kernel.items()))
+    return res
+
+
+def layer_figures(cfg, counts, res):
+    """Rates of one timed workload: tokens/s, effective weight bandwidth,
+    fractions of the HBM and bf16 MFMA peaks, and the same for each
+    contraction (mean of its per-call event times)."""
+    T, H, I, k = cfg.T, cfg.H, cfg.I, cfg.k
+    alg = _algorithmic_bytes(cfg, counts)
+    touched = alg["touched"]
+    w13 = 2 * I * H // 2 + 2 * I * H // 32
+    w2 = H * I // 2 + H * I // 32
+    layer_bytes = touched * (w13 + w2)
+    ms = res["ms_per_step"]
+    per_step = res["per_step"]
+    eff = layer_bytes / (ms * 1e-3) / 1e9
+    out = {"tokens": T, "touched_experts": touched, "weight_bytes_touched": layer_bytes,
+           "ms_per_step": round(ms, 5),
+           "ms_per_step_p10": round(float(np.percentile(per_step, 10)), 5),
+           "ms_per_step_median": round(float(np.median(per_step)), 5),
+           "ms_per_step_p90": round(float(np.percentile(per_step, 90)), 5),
+           "tokens_per_s": round(T / (ms * 1e-3), 1),
+           "effective_weight_GBps": round(eff, 1),
+           "hbm_frac_layer": round(eff / HBM_PEAK_GBPS, 4),
+           "mfma_frac_layer": round(6.0 * T * k * H * I / (ms * 1e-3) / 1e12 /
+                                    BF16_MFMA_PEAK_TFLOPS, 4)}
+    for entry, part, fl in (("moe_mxfp4_gate_up_swiglu", "gate_up", 4.0),
+                            ("moe_mxfp4_down", "down", 2.0)):
+        t = float(np.mean(res["per_kernel"][part]))
+        nbytes, flops = alg[entry], fl * T * k * H * I
+        if flops / nbytes < BF16_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9):
+            ach = nbytes / (t * 1e-3) / 1e9
+            r = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
+                 "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4)}
+        else:
+            ach = flops / (t * 1e-3) / 1e12
+            r = {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_MFMA_PEAK_TFLOPS,
+                 "unit": "TFLOP/s", "frac": round(ach / BF16_MFMA_PEAK_TFLOPS, 4)}
+        r.update({"kernel": entry, "algorithmic_bytes": int(nbytes), "algorithmic_flops": flops,
+                  "mean_launch_ms": round(t, 5),
+                  "median_launch_ms": round(float(np.median(res["per_kernel"][part])), 5),
+                  "traffic": measured_traffic(entry, cfg.name)})
+        out[part] = r
+    return out
+
+
+def stream_probe(args, torch, mm):
+    """Streaming-read ceiling: mxm_stream_xor over a buffer 16x the last-level
+    cache, default cache policy and non-temporal loads."""
+    dev = torch.device("cuda:0")
+    nbytes = 16 * LLC_BYTES
+    steps = args.steps or 20
+    warmup = args.warmup if args.warmup is not None else 5
+    src = torch.randint(-2 ** 31, 2 ** 31 - 1, (nbytes // 4,), dtype=torch.int32, device=dev)
+    want = int(np.bitwise_xor.reduce(src.cpu().numpy().view(np.uint32)))
+    res = torch.zeros(1, dtype=torch.int32, device=dev)
+    s = torch.cuda.current_stream()
+    out = {}
+    for nt in (0, 1):
+        for _ in range(warmup):
+            mm.mxm_stream_xor(src, res, nt)
+        torch.cuda.synchronize()
+        res.zero_()
+        torch.cuda.synchronize()
+        mm.mxm_stream_xor(src, res, nt)
+        torch.cuda.synchronize()
+        ok = (int(res.item()) & 0xffffffff) == want
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        evs[0].record(s)
+        for i in range(steps):
+            mm.mxm_stream_xor(src, res, nt)
+            evs[i + 1].record(s)
+        torch.cuda.synchronize()
+        t = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(steps)])
+        gbps = nbytes / (np.median(t) * 1e-3) / 1e9
+        out["nontemporal" if nt else "default"] = {
+            "GBps_median": round(gbps, 1), "GBps_best": round(nbytes / (t.min() * 1e-3) / 1e9, 1),
+            "frac": round(gbps / HBM_PEAK_GBPS, 4), "ms_median": round(float(np.median(t)), 4),
+            "xor_checked": ok}
+        log("stream probe (%s): %.1f GB/s median, xor %s"
+            % ("non-temporal" if nt else "default", gbps, "ok" if ok else "MISMATCH"))
+    best = max(v["GBps_median"] for v in out.values())
+    print(json.dumps({
+        "metric": "streaming HBM read GB/s on 1 MI355X", "value": best, "unit": "GB/s",
+        "n_gpus": 1, "steps": steps, "warmup": warmup, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "u32", "data": "synthetic",
+        "config": {"workload": "stream_xor %d MiB" % (nbytes >> 20), "bytes": nbytes},
+        "roofline": {"kernel": "mxm_stream_xor", "bound": "hbm", "achieved": best,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(best / HBM_PEAK_GBPS, 4),
+                     "traffic": None},
+        "policies": out, "cpu_baseline": None}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--warm-seconds", type=float, default=1.0,
+                    help="minimum warm-up time per workload, after the --warmup steps")
     ap.add_argument("--config", default="verify_t8")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="time only --config (by default the verify_t8 run also times "
+                         "verify_t64, zipf_t512 and prefill_t8192 on the same weights)")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for cpu_baseline (0 disables)")
-    ap.add_argument("--breakdown", action="store_true", help="per-kernel times on stderr")
     ap.add_argument("--router", action="store_true",
                     help="time moe_router_topk (router projection + top-k) instead of the layer")
     ap.add_argument("--verify", action="store_true",
                     help="time dflash_verify_accept on the workload's sequences (T / 8 blocks of 8)")
+    ap.add_argument("--stream-probe", action="store_true",
+                    help="time the streaming-read probe (the HBM read ceiling) instead")
     ap.add_argument("--save-counts", default=None,
                     help="write the per-expert row counts of the workload to this .npy")
     ap.add_argument("--summarize", action="store_true",
-                    help="summarise rocprofv3 output (no GPU): --stats-dir, --fetch-dir, "
-                         "--write-dir, --counts, --command")
+                    help="summarise rocprofv3 output (no GPU): --stats-dir or --trace-dir, "
+                         "--fetch-dir, --write-dir, --counts, --command")
     ap.add_argument("--stats-dir", default=None)
+    ap.add_argument("--trace-dir", default=None)
+    ap.add_argument("--phases", default=None,
+                    help="with --trace-dir: comma-separated workload names, in run order")
     ap.add_argument("--fetch-dir", default=None)
     ap.add_argument("--write-dir", default=None)
     ap.add_argument("--counts", default=None)
@@ -348,7 +697,6 @@ def main():
     import torch
 
     import mxfp4_moe_expert_route_amd as mm
-    import workloads
 
     cfg = workloads.CONFIGS[args.config]
     if args.router:
@@ -357,137 +705,74 @@ def main():
     if args.verify:
         bench_verify(args, cfg, torch, mm, workloads)
         return
+    mm._lib.lib()
+    if args.stream_probe:
+        stream_probe(args, torch, mm)
+        return
     steps = args.steps or (200 if cfg.T <= 512 else 30)
     warmup = args.warmup if args.warmup is not None else (20 if cfg.T <= 512 else 5)
     dev = torch.device("cuda:0")
-    mm._lib.lib()
 
-    t0 = time.perf_counter()
-    whost = workloads.all_weights(cfg, 0)
-    x_bits = workloads.gen_x_bits(cfg, 0)
-    logits_h = workloads.gen_logits(cfg, x_bits, 0)
-    log("inputs generated in %.1f s (%.2f GB of expert weights)"
-        % (time.perf_counter() - t0, cfg.E * cfg.expert_bytes() / 1e9))
-    names = ("w13_codes", "w13_scales", "w2_codes", "w2_scales")
-    w0 = {k: torch.from_numpy(whost[k]).to(dev) for k in names}
-    w1 = {k: v.clone() for k, v in w0.items()}           # second copy for cache rotation
-    wsets = (w0, w1)
-    x = torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16).to(dev)
-    logits = torch.from_numpy(logits_h).to(dev)
-    T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
-    b = mm.LayerBuffers(T, H, I, E, k, dev)
-    stream = torch.cuda.current_stream()
-
-    def step(i, ev=None):
-        w = wsets[i & 1]
-        mm.moe_route_permute(logits, k, b.topk_ids, b.topk_w, b.counts, b.offsets,
-                             b.sorted_pairs, b.pair_to_row, b.workspace)
-        if ev is not None:
-            ev[0].record(stream)
-        mm.moe_mxfp4_gate_up_swiglu(x, b.sorted_pairs, b.offsets, k, w["w13_codes"],
-                                    w["w13_scales"], b.h)
-        if ev is not None:
-            ev[1].record(stream)
-        mm.moe_mxfp4_down(b.h, b.offsets, k, w["w2_codes"], w["w2_scales"], b.y)
-        mm.moe_combine(b.y, b.topk_w, b.pair_to_row, b.out)
-
-    for i in range(warmup):
-        step(i)
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t_start.record(stream)
-    for i in range(steps):
-        step(i, evs[i])
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_step = t_start.elapsed_time(t_end) / steps
-    gu_ms = float(np.mean([a.elapsed_time(bb) for a, bb in evs]))
-    log("wall %.3f ms/step, events %.3f ms/step, gate_up %.3f ms"
-        % (wall * 1e3 / steps, ms_step, gu_ms))
-
-    counts = b.counts.cpu().numpy()
+    whost, wsets = upload_weights(cfg, torch, dev)
+    clocks = ClockSampler(torch)
+    run = LayerRun(cfg, wsets, torch, mm, dev)
+    res = time_layer(run, steps, warmup, args.warm_seconds, clocks)
+    counts = run.b.counts.cpu().numpy()
     if args.save_counts:
         np.save(args.save_counts, counts)
-    touched = int((counts > 0).sum())
-    w13_bytes = 2 * I * H // 2 + 2 * I * H // 32
-    w2_bytes = H * I // 2 + H * I // 32
-    layer_weight_bytes = touched * (w13_bytes + w2_bytes)
-    gu_bytes = touched * w13_bytes + T * H * 2          # weights streamed + x read once
-    flops = 6.0 * T * k * H * I
-    eff_gbps = layer_weight_bytes / (ms_step * 1e-3) / 1e9
-    gu_gbps = gu_bytes / (gu_ms * 1e-3) / 1e9
-    tokens_per_s = T / (ms_step * 1e-3)
-
-    if args.breakdown:
-        names_k = ("route+permute", "gate_up", "down", "combine")
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(20)]
-        for r in range(20):
-            w = wsets[r & 1]
-            e = ev[r]
-            e[0].record(stream)
-            mm.moe_route_permute(logits, k, b.topk_ids, b.topk_w, b.counts, b.offsets,
-                                 b.sorted_pairs, b.pair_to_row, b.workspace)
-            e[1].record(stream)
-            mm.moe_mxfp4_gate_up_swiglu(x, b.sorted_pairs, b.offsets, k, w["w13_codes"],
-                                        w["w13_scales"], b.h)
-            e[2].record(stream)
-            mm.moe_mxfp4_down(b.h, b.offsets, k, w["w2_codes"], w["w2_scales"], b.y)
-            e[3].record(stream)
-            mm.moe_combine(b.y, b.topk_w, b.pair_to_row, b.out)
-            e[4].record(stream)
-        torch.cuda.synchronize()
-        for i, n in enumerate(names_k):
-            t = np.median([ev[r][i].elapsed_time(ev[r][i + 1]) for r in range(20)])
-            log("  %-8s %8.1f us" % (n, t * 1e3))
+    fig = layer_figures(cfg, counts, res)
 
     cpu = None
     if args.cpu_budget > 0:
-        cpu = cpu_baseline(cfg, x_bits, logits_h, whost, args.cpu_budget)
+        cpu = cpu_baseline(cfg, run.x_bits, run.logits_h, whost, args.cpu_budget)
         log("cpu baseline: %.3f tokens/s (%s)" % (cpu["value"], cpu["sample"]))
+    del whost
 
-    traffic = measured_traffic("moe_mxfp4_gate_up_swiglu", cfg.name)
-    # the gate/up contraction is bound by HBM when its flops per algorithmic
-    # byte are below the machine balance (bf16 MFMA peak / HBM peak), else by
-    # the matrix cores
-    gu_flops = 4.0 * T * k * H * I
-    if gu_flops / gu_bytes < BF16_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9):
-        roofline = {"kernel": "moe_mxfp4_gate_up_swiglu", "bound": "hbm",
-                    "achieved": round(gu_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                    "frac": round(gu_gbps / HBM_PEAK_GBPS, 4)}
-    else:
-        tflops = gu_flops / (gu_ms * 1e-3) / 1e12
-        roofline = {"kernel": "moe_mxfp4_gate_up_swiglu", "bound": "mfma",
-                    "achieved": round(tflops, 1), "peak": BF16_MFMA_PEAK_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4)}
-    roofline.update({"traffic": traffic, "algorithmic_bytes": gu_bytes,
-                     "algorithmic_flops": gu_flops, "mean_launch_ms": round(gu_ms, 5)})
+    extra = {}
+    if not args.no_extra and cfg.name == "verify_t8":
+        del run
+        for name in EXTRA_WORKLOADS:
+            c2 = workloads.CONFIGS[name]
+            assert c2.lid == cfg.lid and (c2.H, c2.I, c2.E, c2.k) == (cfg.H, cfg.I, cfg.E, cfg.k)
+            r2 = LayerRun(c2, wsets, torch, mm, dev)
+            res2 = time_layer(r2, steps, warmup, args.warm_seconds)
+            extra[name] = layer_figures(c2, r2.b.counts.cpu().numpy(), res2)
+            del r2
+            torch.cuda.empty_cache()
+
+    roofline = dict(fig["gate_up"])
     line = {
         "metric": METRIC,
-        "value": round(tokens_per_s, 1),
+        "value": fig["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": steps,
         "warmup": warmup,
-        "ms_per_step": round(ms_step, 5),
+        "ms_per_step": fig["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": cfg.name, "tokens": T, "hidden": H, "intermediate": I,
-                   "experts": E, "top_k": k, "weight_format": "mxfp4 (E2M1, E8M0 per 32)",
-                   "touched_experts": touched, "weight_bytes_touched": layer_weight_bytes,
+        "config": {"workload": cfg.name, "tokens": cfg.T, "hidden": cfg.H,
+                   "intermediate": cfg.I, "experts": cfg.E, "top_k": cfg.k,
+                   "weight_format": "mxfp4 (E2M1, E8M0 per 32)",
+                   "touched_experts": fig["touched_experts"],
+                   "weight_bytes_touched": fig["weight_bytes_touched"],
                    "seed": 0, "parallelism": "none (1 GPU)"},
-        "effective_weight_GBps": round(eff_gbps, 1),
-        "hbm_frac_layer": round(eff_gbps / HBM_PEAK_GBPS, 4),
-        "mfma_frac_layer": round(flops / (ms_step * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+        "effective_weight_GBps": fig["effective_weight_GBps"],
+        "hbm_frac_layer": fig["hbm_frac_layer"],
+        "mfma_frac_layer": fig["mfma_frac_layer"],
+        "ms_per_step_p10": fig["ms_per_step_p10"],
+        "ms_per_step_median": fig["ms_per_step_median"],
+        "ms_per_step_p90": fig["ms_per_step_p90"],
+        "warmup_steps_run": res["warmup_steps"],
+        "warmup_s": round(res["warmup_s"], 2),
         "roofline": roofline,
+        "down": fig["down"],
+        "workloads": extra,
+        "clocks": clocks.summary(),
+        "host_cpu": host_cpu_model(),
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

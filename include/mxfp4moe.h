@@ -271,6 +271,17 @@ int moe_mxfp4_layer(const uint16_t* x_bf16, const float* logits, int T, int H,
                     int32_t* pair_to_row, uint16_t* h_bf16, float* y, float* out,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * mxm_stream_xor — measurement aid, not a step of the layer: a plain
+ * streaming read of `bytes` bytes at `src` (16-byte aligned, bytes % 16 == 0)
+ * that XORs every 32-bit word into *result (4-byte aligned; the caller sets
+ * it beforehand, the call XORs into it).  The rate it reaches is the HBM read
+ * ceiling the weight-streaming contractions are compared with; nontemporal
+ * != 0 issues the loads with the non-temporal hint.
+ */
+int mxm_stream_xor(const void* src, int64_t bytes, int nontemporal, uint32_t* result,
+                   void* stream);
+
 #ifdef __cplusplus
 }
 #endif

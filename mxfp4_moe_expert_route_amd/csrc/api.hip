@@ -28,7 +28,9 @@ int check_ffn_shape(int T, int H, int I, int E, int k) {
   const int st = check_route_shape(T, E, k);
   if (st != MXM_OK) return st;
   if (H < 32 || I < 32 || H % 32 || I % 32) return MXM_ERR_SHAPE;
-  // per-wave scale staging in LDS must fit a workgroup's 64 KB
+  // the streaming kernels stage every wave's scale rows in LDS: 8 H bytes
+  // for gate/up (128 KB at H = 16384, the most a workgroup may hold) and 8 I
+  // bytes for down
   if (H > kMaxH || I > kMaxI) return MXM_ERR_SHAPE;
   // weight element counts per expert must fit the kernels' size_t math and the
   // activation rows their int32 row indices
@@ -303,6 +305,15 @@ int moe_mxfp4_layer(const uint16_t* x_bf16, const float* logits, int T, int H, i
       MXM_OK)
     return st;
   return moe_combine(y, topk_w, pair_to_row, T, H, k, out, stream);
+}
+
+int mxm_stream_xor(const void* src, int64_t bytes, int nontemporal, uint32_t* result,
+                   void* stream) {
+  if (bytes < 0 || bytes % 16) return MXM_ERR_SHAPE;
+  if (bytes == 0) return MXM_OK;
+  if (!src || !result) return MXM_ERR_NULL;
+  if (!aligned(src, 16) || !aligned(result, 4)) return MXM_ERR_ALIGN;
+  return launched(mxm::launch_stream_xor(src, bytes, nontemporal, result, as_stream(stream)));
 }
 
 }  // extern "C"

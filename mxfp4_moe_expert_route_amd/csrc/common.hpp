@@ -173,6 +173,9 @@ size_t verify_workspace_bytes(int B, int L);
 hipError_t launch_verify(const float* target, const float* draft, const int32_t* tokens,
                          const float* uniforms, int B, int L, int V, int32_t* accept_len,
                          int32_t* next_token, void* workspace, hipStream_t s);
+// XOR of every 32-bit word of src into *result (streaming-read probe).
+hipError_t launch_stream_xor(const void* src, int64_t bytes, int nontemporal, uint32_t* result,
+                             hipStream_t s);
 hipError_t launch_combine(const float* y, const float* w, const int32_t* pair_to_row, int T,
                           int H, int k, float* out, hipStream_t s);
 

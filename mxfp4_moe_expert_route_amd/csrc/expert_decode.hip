@@ -50,9 +50,6 @@ typedef __attribute__((ext_vector_type(4))) int int4v;
 // vmcnt low bits 3:0, high bits 15:14; expcnt 6:4 and lgkmcnt 11:8 at max).
 #define MXM_VMCNT(n) ((((n) & 15) | (((n) >> 4) << 14)) | (7 << 4) | (15 << 8))
 
-#ifndef MXM_DEC_RING
-#define MXM_DEC_RING 4
-#endif
 constexpr int kMW = 4;                          // MFMA waves
 constexpr int kCW = 2;                          // code loader waves
 constexpr int kThreadsDec = (kMW + kCW + 2) * kWave;   // + activation and scale loaders
@@ -62,7 +59,7 @@ constexpr int kChunkK = 512;                    // K elements per stage
 constexpr int kTokRows = 16;                    // token rows per tile
 constexpr int kStageB = kGroupRows * kChunkK / 2;   // 16 KB of codes
 constexpr int kPerLoader = kStageB / 1024 / kCW;    // loads per code loader per stage
-constexpr int kRing = MXM_DEC_RING;
+constexpr int kRing = 4;                        // code stages in flight
 // cache policy of the code loads: non-temporal.  Each code byte is read
 // once, and the hinted stream runs faster (verify_t8: gate/up 141.6 -> 126.9
 // us, down 79.0 -> 67.4 us; the measured HBM traffic also fell, to 1.002x

@@ -69,10 +69,7 @@ constexpr int kKS = 64;              // K per stage (2 MX blocks)
 constexpr int kRingA = 3;            // activation stages in the LDS ring
 constexpr int kSS = 4;               // stages per weight super-stage (128 code bytes per row)
 constexpr int kRingW = 2;            // weight super-stage slots
-#ifndef MXM_DENSE_WAVES
-#define MXM_DENSE_WAVES 8
-#endif
-constexpr int kWaves = MXM_DENSE_WAVES;
+constexpr int kWaves = 8;            // two per SIMD
 constexpr int kDThreads = kWaves * kWave;
 constexpr int kMinRows = 64;         // experts with fewer rows use the streaming kernels
 constexpr int kMaxE = 1024;

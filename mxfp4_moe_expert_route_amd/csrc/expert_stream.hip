@@ -37,16 +37,10 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
 
-// Tunables (compile-time; the defaults are the measured best on MI355X).
-#ifndef MXM_WDEPTH
-#define MXM_WDEPTH 2        // fragments in flight per wave
-#endif
-#ifndef MXM_GU_NSUB
-#define MXM_GU_NSUB 2       // 16-column intermediate subtiles per wave (gate/up)
-#endif
-#ifndef MXM_DN_NSUB
-#define MXM_DN_NSUB 4       // 16-row output subtiles per wave (down)
-#endif
+// Tile shape (the measured best on MI355X).
+constexpr int kWDepth = 2;          // fragments in flight per wave
+constexpr int kGuNsub = 2;          // 16-column intermediate subtiles per wave (gate/up)
+constexpr int kDnNsub = 4;          // 16-row output subtiles per wave (down)
 
 // One step of a lane's streams: one MX block (16 code bytes) of each weight
 // subtile and the 32 matching bf16 activations of each row subtile.
@@ -57,7 +51,7 @@ struct Frag {
 };
 
 // Loads are unconditional (addresses clamped in bounds) so that no branch
-// separates them: the compiler then keeps MXM_WDEPTH steps in flight instead
+// separates them: the compiler then keeps kWDepth steps in flight instead
 // of draining the load queue before every step.  Rows past the tile's end
 // read a valid row whose output column is never stored.
 template <int NA, int MS>
@@ -128,7 +122,7 @@ __device__ __forceinline__ void stage_scales(const uint8_t* const (&ws0)[NA], in
 }
 
 // acc[a][m] += W_a (16 rows x K) . X_m (16 rows x K)^T over all nblk MX blocks,
-// with MXM_WDEPTH steps of code/activation loads in flight.  The step count is
+// with kWDepth steps of code/activation loads in flight.  The step count is
 // padded to a multiple of the depth with zero-scale steps so the ring of
 // fragments has compile-time indices and the loop body has no branch.
 template <int NA, int MS>
@@ -137,7 +131,7 @@ __device__ __forceinline__ void stream_k(const uint8_t* const (&wc)[NA],
                                          const uint8_t* const (&sl)[NA],
                                          const uint16_t* const (&xr)[MS], int nblk,
                                          f32x4 (&acc)[NA][MS]) {
-  constexpr int D = MXM_WDEPTH;
+  constexpr int D = kWDepth;
   const int g = lane_id() >> 4;
   const int nsteps = (((nblk + 3) >> 2) + D - 1) / D * D;
   Frag<NA, MS> f[D];
@@ -147,14 +141,6 @@ __device__ __forceinline__ void stream_k(const uint8_t* const (&wc)[NA],
   // the first fragments and the scale copy land together
   __builtin_amdgcn_s_waitcnt(MXM_VMCNT(0));
   for (int s0 = 0; s0 < nsteps; s0 += D) {
-#ifdef MXM_PRIO
-    // issue priority falls as the wave progresses, so that the waves of a
-    // SIMD move together instead of oldest-first
-    if (s0 == 0) __builtin_amdgcn_s_setprio(3);
-    else if (s0 == ((nsteps >> 2) & ~(D - 1))) __builtin_amdgcn_s_setprio(2);
-    else if (s0 == ((nsteps >> 1) & ~(D - 1))) __builtin_amdgcn_s_setprio(1);
-    else if (s0 == ((3 * nsteps >> 2) & ~(D - 1))) __builtin_amdgcn_s_setprio(0);
-#endif
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       mma_frag<NA, MS>(f[d], sl, 4 * (s0 + d) + g, nblk, acc);
@@ -326,11 +312,20 @@ template <int MS>
 hipError_t gate_up_ms(const uint16_t* x, const int32_t* sp, const int32_t* off, int T, int H,
                       int I, int E, int k, const uint8_t* c, const uint8_t* sc, uint16_t* h,
                       int hi, hipStream_t s) {
-  constexpr int NSUB = MXM_GU_NSUB;
+  constexpr int NSUB = kGuNsub;
   const int R = T * k;
   const int ntile_n = (I + kWaves * 16 * NSUB - 1) / (kWaves * 16 * NSUB);
   const unsigned grid = stream_grid(int64_t(tile_slots(R, E, 16 * MS)) * ntile_n);
+  // 8 H bytes of scales: above 64 KB (H > 8192) the kernel's LDS limit is
+  // raised to the 128 KB that H = 16384 needs
   const size_t lds = size_t(kWaves) * 2 * NSUB * 16 * (H / 32);
+  static std::atomic<bool> lds_set[kMaxDevices];
+  if (lds > 65536) {
+    const hipError_t e = lds_limit_once(reinterpret_cast<const void*>(&k_gate_up<MS, NSUB>),
+                                        int(size_t(kWaves) * 2 * NSUB * 16 * (16384 / 32)),
+                                        lds_set);
+    if (e != hipSuccess) return e;
+  }
   k_gate_up<MS, NSUB><<<dim3(grid), kThreads, lds, s>>>(x, sp, off, H, I, E, k, c, sc,
                                                                     h, ntile_n, hi);
   return hipGetLastError();
@@ -339,7 +334,7 @@ hipError_t gate_up_ms(const uint16_t* x, const int32_t* sp, const int32_t* off, 
 template <int MS>
 hipError_t down_ms(const uint16_t* h, const int32_t* off, int T, int H, int I, int E, int k,
                    const uint8_t* c, const uint8_t* sc, float* y, int hi, hipStream_t s) {
-  constexpr int NSUB = MXM_DN_NSUB;
+  constexpr int NSUB = kDnNsub;
   const int R = T * k;
   const int ntile_n = (H + kWaves * 16 * NSUB - 1) / (kWaves * 16 * NSUB);
   const unsigned grid = stream_grid(int64_t(tile_slots(R, E, 16 * MS)) * ntile_n);
@@ -356,11 +351,9 @@ hipError_t launch_gate_up(const uint16_t* x, const int32_t* sorted_pairs, const 
                           const uint8_t* scales, uint16_t* h, int hi, hipStream_t s) {
   switch (choose_ms(T * k, E)) {
     case 1:
-#ifndef MXM_NO_DECODE
       if (decode_supported(T, H, I, E, k))
         return launch_gate_up_decode(x, sorted_pairs, offsets, T, H, I, E, k, codes, scales, h, hi,
                                      s);
-#endif
       return gate_up_ms<1>(x, sorted_pairs, offsets, T, H, I, E, k, codes, scales, h, hi, s);
     case 2: return gate_up_ms<2>(x, sorted_pairs, offsets, T, H, I, E, k, codes, scales, h, hi, s);
     default: return gate_up_ms<4>(x, sorted_pairs, offsets, T, H, I, E, k, codes, scales, h, hi, s);
@@ -372,10 +365,8 @@ hipError_t launch_down(const uint16_t* h, const int32_t* offsets, int T, int H, 
                        hipStream_t s) {
   switch (choose_ms(T * k, E)) {
     case 1:
-#ifndef MXM_NO_DECODE
       if (decode_supported(T, H, I, E, k))
         return launch_down_decode(h, offsets, T, H, I, E, k, codes, scales, y, hi, s);
-#endif
       return down_ms<1>(h, offsets, T, H, I, E, k, codes, scales, y, hi, s);
     case 2: return down_ms<2>(h, offsets, T, H, I, E, k, codes, scales, y, hi, s);
     default: return down_ms<4>(h, offsets, T, H, I, E, k, codes, scales, y, hi, s);

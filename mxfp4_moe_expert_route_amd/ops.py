@@ -270,3 +270,16 @@ def moe_mxfp4_layer(x, logits, k, w13_codes, w13_scales, w2_codes, w2_scales, bu
         _ptr(b.sorted_pairs), _ptr(b.pair_to_row), _ptr(b.h), _ptr(b.y), _ptr(b.out),
         _ptr(b.workspace), b.workspace.numel(), _stream()), "moe_mxfp4_layer")
     return b
+
+
+def mxm_stream_xor(src, result, nontemporal=False):
+    """Streaming-read probe (a measurement aid): XOR every 32-bit word of the
+    contiguous tensor `src` (byte size a multiple of 16) into `result`, an
+    int32 tensor of one element that the caller initialises."""
+    if not isinstance(src, torch.Tensor) or src.device.type != "cuda" or not src.is_contiguous():
+        raise ValueError("src must be a contiguous GPU tensor")
+    _need(result, "result", torch.int32, (1,), src.device)
+    nbytes = src.numel() * src.element_size()
+    check(lib().mxm_stream_xor(_ptr(src), nbytes, 1 if nontemporal else 0, _ptr(result),
+                               _stream()), "mxm_stream_xor")
+    return result
