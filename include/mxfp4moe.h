@@ -57,7 +57,8 @@ enum mxm_status {
   MXM_ERR_ALIGN = -4,         /* a pointer is not aligned as stated above */
   MXM_ERR_LAUNCH = -5,        /* a kernel launch failed (HIP error) */
   MXM_ERR_UNIMPLEMENTED = -6, /* reserved */
-  MXM_ERR_WORKSPACE = -7      /* workspace smaller than the call needs */
+  MXM_ERR_WORKSPACE = -7,     /* workspace smaller than the call needs */
+  MXM_ERR_SCRATCH = -8        /* moe_mxfp4_layer_noalloc: sizes need more than its fixed scratch */
 };
 
 enum mxm_dtype { MXM_F32 = 0, MXM_BF16 = 1 };
@@ -270,6 +271,30 @@ int moe_mxfp4_layer(const uint16_t* x_bf16, const float* logits, int T, int H,
                     int32_t* counts, int32_t* offsets, int32_t* sorted_pairs,
                     int32_t* pair_to_row, uint16_t* h_bf16, float* y, float* out,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * moe_mxfp4_layer_noalloc — moe_mxfp4_layer for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same arguments without the
+ * workspace, the same kernels and results.
+ *   The grouping workspace (needed above 8192 token-expert pairs, see
+ *   moe_permute_workspace_bytes) lives in a fixed 1 MiB device array of the
+ *   library, one per GPU, held until the process ends; its address is looked
+ *   up on the first call on each device.  Sizes whose workspace exceeds
+ *   1 MiB return MXM_ERR_SCRATCH with nothing enqueued (E = 384 takes up to
+ *   682 ranges of 1024 pairs, i.e. T*k up to 698,368).  The call allocates
+ *   and frees nothing.  Every call on one GPU shares that array: calls that
+ *   overlap on one GPU (two streams, or two host threads) race and must be
+ *   ordered by the caller.  Inputs, outputs and intermediates are the
+ *   caller's, as for moe_mxfp4_layer.
+ */
+int moe_mxfp4_layer_noalloc(const uint16_t* x_bf16, const float* logits, int T, int H,
+                            int I, int E, int k, const uint8_t* w13_codes,
+                            const uint8_t* w13_scales, const uint8_t* w2_codes,
+                            const uint8_t* w2_scales, int32_t* topk_ids, float* topk_w,
+                            int32_t* counts, int32_t* offsets, int32_t* sorted_pairs,
+                            int32_t* pair_to_row, uint16_t* h_bf16, float* y, float* out,
+                            void* stream);
 
 /*
  * mxm_stream_xor — measurement aid, not a step of the layer: a plain

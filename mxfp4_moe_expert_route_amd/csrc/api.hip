@@ -40,6 +40,46 @@ int check_ffn_shape(int T, int H, int I, int E, int k) {
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
+// Null and alignment checks of the layer call's buffers.
+int check_layer_pointers(const uint16_t* x_bf16, const float* logits, const uint8_t* w13_codes,
+                         const uint8_t* w13_scales, const uint8_t* w2_codes,
+                         const uint8_t* w2_scales, const int32_t* topk_ids, const float* topk_w,
+                         const int32_t* counts, const int32_t* offsets,
+                         const int32_t* sorted_pairs, const int32_t* pair_to_row,
+                         const uint16_t* h_bf16, const float* y, const float* out) {
+  if (!x_bf16 || !logits || !w13_codes || !w13_scales || !w2_codes || !w2_scales || !topk_ids ||
+      !topk_w || !counts || !offsets || !sorted_pairs || !pair_to_row || !h_bf16 || !y || !out)
+    return MXM_ERR_NULL;
+  if (!aligned(x_bf16, 16) || !aligned(w13_codes, 16) || !aligned(w2_codes, 16) ||
+      !aligned(w13_scales, 16) || !aligned(w2_scales, 16) || !aligned(h_bf16, 16) ||
+      !aligned(y, 16) || !aligned(out, 16) || !aligned(logits, 4) || !aligned(topk_ids, 4) ||
+      !aligned(topk_w, 4) || !aligned(counts, 4) || !aligned(offsets, 4) ||
+      !aligned(sorted_pairs, 4) || !aligned(pair_to_row, 4))
+    return MXM_ERR_ALIGN;
+  return MXM_OK;
+}
+
+// Scratch of moe_mxfp4_layer_noalloc: the grouping workspace (per-range
+// expert histograms, then per-range bases) in a fixed device array, one copy
+// per GPU, held until the process ends.  Host code uses the device address
+// hipGetSymbolAddress returns for the current device, never the array's
+// name (a host-side stand-in).
+constexpr size_t kScratchBytes = size_t(1) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+std::atomic<void*> scratch_ptr[mxm::kMaxDevices];
+
+// This device's copy of `scratch` (looked up on the first call per device);
+// nullptr when the address cannot be had.
+void* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= mxm::kMaxDevices) return nullptr;
+  void* p = scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+  scratch_ptr[dev].store(p, std::memory_order_release);
+  return p;
+}
+
 // Experts with many rows go to the LDS-tiled dense kernel, the rest to the
 // streaming kernel.  Chosen from host-known sizes only: the dense pass is
 // worth a launch when the mean rows per touched expert is at least 8 (so
@@ -97,6 +137,9 @@ const char* mxm_status_string(int status) {
     case MXM_ERR_LAUNCH: return "MXM_ERR_LAUNCH: a HIP kernel launch failed";
     case MXM_ERR_UNIMPLEMENTED: return "MXM_ERR_UNIMPLEMENTED";
     case MXM_ERR_WORKSPACE: return "MXM_ERR_WORKSPACE: workspace too small";
+    case MXM_ERR_SCRATCH:
+      return "MXM_ERR_SCRATCH: the call needs more scratch than the library's fixed 1 MiB "
+             "device buffer holds";
     default: return "unknown mxfp4moe status";
   }
 }
@@ -287,14 +330,10 @@ int moe_mxfp4_layer(const uint16_t* x_bf16, const float* logits, int T, int H, i
   if (st != MXM_OK) return st;
   if (workspace_bytes < moe_permute_workspace_bytes(T, E, k)) return MXM_ERR_WORKSPACE;
   if (T == 0) return MXM_OK;
-  if (!x_bf16 || !logits || !w13_codes || !w13_scales || !w2_codes || !w2_scales || !topk_ids ||
-      !topk_w || !counts || !offsets || !sorted_pairs || !pair_to_row || !h_bf16 || !y || !out)
-    return MXM_ERR_NULL;
-  if (!aligned(x_bf16, 16) || !aligned(w13_codes, 16) || !aligned(w2_codes, 16) ||
-      !aligned(w13_scales, 16) || !aligned(w2_scales, 16) || !aligned(h_bf16, 16) || !aligned(y, 16) || !aligned(out, 16) || !aligned(logits, 4) ||
-      !aligned(topk_ids, 4) || !aligned(topk_w, 4) || !aligned(counts, 4) ||
-      !aligned(offsets, 4) || !aligned(sorted_pairs, 4) || !aligned(pair_to_row, 4))
-    return MXM_ERR_ALIGN;
+  if ((st = check_layer_pointers(x_bf16, logits, w13_codes, w13_scales, w2_codes, w2_scales,
+                                 topk_ids, topk_w, counts, offsets, sorted_pairs, pair_to_row,
+                                 h_bf16, y, out)) != MXM_OK)
+    return st;
   if ((st = moe_route_permute(logits, T, E, k, topk_ids, topk_w, counts, offsets, sorted_pairs,
                               pair_to_row, workspace, workspace_bytes, stream)) != MXM_OK)
     return st;
@@ -305,6 +344,30 @@ int moe_mxfp4_layer(const uint16_t* x_bf16, const float* logits, int T, int H, i
       MXM_OK)
     return st;
   return moe_combine(y, topk_w, pair_to_row, T, H, k, out, stream);
+}
+
+int moe_mxfp4_layer_noalloc(const uint16_t* x_bf16, const float* logits, int T, int H, int I,
+                            int E, int k, const uint8_t* w13_codes, const uint8_t* w13_scales,
+                            const uint8_t* w2_codes, const uint8_t* w2_scales, int32_t* topk_ids,
+                            float* topk_w, int32_t* counts, int32_t* offsets,
+                            int32_t* sorted_pairs, int32_t* pair_to_row, uint16_t* h_bf16,
+                            float* y, float* out, void* stream) {
+  int st = check_ffn_shape(T, H, I, E, k);
+  if (st != MXM_OK) return st;
+  const size_t need = moe_permute_workspace_bytes(T, E, k);
+  if (need > kScratchBytes) return MXM_ERR_SCRATCH;
+  if (T == 0) return MXM_OK;
+  if ((st = check_layer_pointers(x_bf16, logits, w13_codes, w13_scales, w2_codes, w2_scales,
+                                 topk_ids, topk_w, counts, offsets, sorted_pairs, pair_to_row,
+                                 h_bf16, y, out)) != MXM_OK)
+    return st;
+  void* ws = nullptr;
+  if (need > 0 && !(ws = scratch_on_current_device())) return MXM_ERR_LAUNCH;
+  // the grouping kernels overwrite every workspace word they later read, so
+  // the previous call's contents need no clearing
+  return moe_mxfp4_layer(x_bf16, logits, T, H, I, E, k, w13_codes, w13_scales, w2_codes,
+                         w2_scales, topk_ids, topk_w, counts, offsets, sorted_pairs, pair_to_row,
+                         h_bf16, y, out, ws, need, stream);
 }
 
 int mxm_stream_xor(const void* src, int64_t bytes, int nontemporal, uint32_t* result,

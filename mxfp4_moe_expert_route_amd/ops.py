@@ -272,6 +272,32 @@ def moe_mxfp4_layer(x, logits, k, w13_codes, w13_scales, w2_codes, w2_scales, bu
     return b
 
 
+def moe_mxfp4_layer_noalloc(x, logits, k, w13_codes, w13_scales, w2_codes, w2_scales, buffers):
+    """moe_mxfp4_layer through the entry point that allocates nothing: its
+    grouping workspace is the library's fixed device scratch (the workspace
+    tensor of `buffers` is not used).  `buffers` (LayerBuffers of this shape)
+    must be passed in, so the call itself allocates nothing either."""
+    _need(x, "x", torch.bfloat16)
+    T, H = x.shape
+    E, two_i, _ = w13_codes.shape
+    I = two_i // 2
+    dev = x.device
+    _need(logits, "logits", torch.float32, (T, E), dev)
+    _need(w13_codes, "w13_codes", torch.uint8, (E, 2 * I, H // 2), dev)
+    _need(w13_scales, "w13_scales", torch.uint8, (E, 2 * I, H // 32), dev)
+    _need(w2_codes, "w2_codes", torch.uint8, (E, H, I // 2), dev)
+    _need(w2_scales, "w2_scales", torch.uint8, (E, H, I // 32), dev)
+    b = buffers
+    if (b.T, b.H, b.I, b.E, b.k) != (T, H, I, E, k):
+        raise ValueError("buffers were made for another shape")
+    check(lib().moe_mxfp4_layer_noalloc(
+        _ptr(x), _ptr(logits), T, H, I, E, k, _ptr(w13_codes), _ptr(w13_scales), _ptr(w2_codes),
+        _ptr(w2_scales), _ptr(b.topk_ids), _ptr(b.topk_w), _ptr(b.counts), _ptr(b.offsets),
+        _ptr(b.sorted_pairs), _ptr(b.pair_to_row), _ptr(b.h), _ptr(b.y), _ptr(b.out),
+        _stream()), "moe_mxfp4_layer_noalloc")
+    return b
+
+
 def mxm_stream_xor(src, result, nontemporal=False):
     """Streaming-read probe (a measurement aid): XOR every 32-bit word of the
     contiguous tensor `src` (byte size a multiple of 16) into `result`, an

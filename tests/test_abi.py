@@ -32,7 +32,8 @@ def test_header_declares_the_boundary():
     for n in ("mxfp4_pack", "mxfp4_unpack", "moe_route_topk", "moe_router_topk",
               "dflash_verify_accept", "dflash_verify_workspace_bytes", "moe_permute",
               "moe_permute_workspace_bytes", "moe_route_permute", "moe_mxfp4_gate_up_swiglu", "moe_mxfp4_down",
-              "moe_combine", "moe_mxfp4_layer", "mxm_status_string", "mxm_version"):
+              "moe_combine", "moe_mxfp4_layer", "moe_mxfp4_layer_noalloc", "mxm_stream_xor",
+              "mxm_status_string", "mxm_version"):
         assert n in names
 
 
@@ -44,7 +45,7 @@ def test_every_declared_symbol_is_exported_and_bound(lib):
 
 
 def test_status_strings(lib):
-    for s in range(-7, 1):
+    for s in range(-8, 1):
         assert lib.mxm_status_string(s)
     assert lib.mxm_version() >= 100
 
@@ -143,3 +144,21 @@ def test_python_wrappers_reject_host_tensors():
         mm.mxfp4_pack(torch.zeros(4, 64))
     with pytest.raises(TypeError):
         mm.moe_route_topk(torch.zeros(4, 8, dtype=torch.float64), 2)
+
+
+def test_noalloc_layer_argument_checks(lib):
+    f = lib.moe_mxfp4_layer_noalloc
+    ptrs = [P] * 13
+    # 131072 tokens x top-8 over 1024 experts: 1024 ranges x 4 KB of grouping
+    # workspace, beyond the fixed 1 MiB scratch
+    assert f(P, P, 131072, 6144, 2048, 1024, 8, *ptrs, None) == -8
+    # the largest page-shaped batch that fits: 682 ranges x 384 x 4 B <= 1 MiB;
+    # one pair more needs 683 ranges
+    assert lib.moe_permute_workspace_bytes(87296, 384, 8) <= 1 << 20
+    assert f(P, P, 87297, 6144, 2048, 384, 8, *ptrs, None) == -8
+    assert f(P, P, 0, 6144, 2048, 384, 8, *ptrs, None) == 0                 # empty: no-op
+    assert f(P, P, 8, 6144, 2048, 384, 33, *ptrs, None) == -2       # k > 32
+    assert f(None, P, 8, 6144, 2048, 384, 8, *ptrs, None) == -1             # null x
+    assert f(P + 4, P, 8, 6144, 2048, 384, 8, *ptrs, None) == -4            # misaligned x
+    # nulls are caught before the scratch is looked up, also above 8192 pairs
+    assert f(None, P, 2048, 256, 128, 384, 8, *ptrs, None) == -1
