@@ -29,6 +29,7 @@ SMALL = [
     ("many_e", (64, 256, 64, 1024, 32)),       # most experts empty
     ("wide_k", (300, 2048, 512, 32, 8)),
     ("fused_e960", (16, 256, 64, 960, 32)),   # routing and grouping fused (T <= 16), largest E
+    ("wide_h16384", (4, 16384, 64, 4, 2)),     # largest H: 128 KB of scales in the streaming kernel
 ]
 
 # shapes that take the LDS-tiled dense kernel (H, I multiples of 512, many
@@ -162,13 +163,15 @@ def test_layer_page_shaped_sampled(mm, name, n):
 @pytest.mark.parametrize("name", ["verify_t64", "zipf_t512", "prefill_t8192"])
 def test_page_shaped_every_block_written_and_sampled(mm, name):
     """At full size, in the benchmark's launch configuration: every element of
-    h, y and the output is written (the buffers start as NaN), and h is checked
-    against the oracle at one (row, column) of every block of an expert's rows
-    x 128 columns, the blocks 192 rows long for experts with at least 64 rows
-    and 16 rows long for the others.  These are the work items of the
-    contraction kernels (192 or 16 token rows by 128 gate columns with their up
-    columns), so each item gets one sampled element and a skipped, repeated or
-    misplaced item shows."""
+    h, y and the output is written (the buffers start as NaN), and one element
+    of every work item of every kernel is checked against the oracle:
+      h    every block of an expert's rows x 128 columns (gate/up items: 192
+           token rows for experts with at least 64 rows, 16 for the others, by
+           128 gate columns with their up columns);
+      y    every block of those rows x 256 output features (down items), from
+           the GPU's own h row;
+      out  every token x 2048 columns (combine items), from the GPU's y rows.
+    A skipped, repeated or misplaced item of any kernel shows."""
     from oracle import layer as olayer, mx as omx
     from oracle import permute as operm, route as oroute
     from _gpu import dev_bf16, bf16_ulp_diff
@@ -194,6 +197,7 @@ def test_page_shaped_every_block_written_and_sampled(mm, name):
     ids, _ = oroute.route_topk(logits, k)
     lists = operm.permute(ids, E)
     assert np.array_equal(offs_d.cpu().numpy(), lists["offsets"])
+    assert np.array_equal(p2r_d.cpu().numpy(), lists["pair_to_row"])
     offsets, sorted_pairs = lists["offsets"], lists["sorted_pairs"]
     rng = np.random.default_rng(7)
     rows, cols = [], []
@@ -225,3 +229,48 @@ def test_page_shaped_every_block_written_and_sampled(mm, name):
         % (name, len(rows), 100.0 * (d > 0).mean(), int(d.max())))
     assert np.all(np.abs(hg - hr) <= np.maximum(ulp, 1e-2 * rms)), "h element out of bound"
     assert (d > 1).mean() <= 1e-3
+
+    # y: one element of every down work item, an expert's block of rows (192
+    # or 16, as above) by 256 output features, against the oracle's down row
+    # applied to the GPU's own h row in float64.  fp32 accumulation of I
+    # products is within I * 2^-24 of their absolute sum; the bound is twice
+    # that, far below what a misplaced or stale item would show.
+    h_all = h.view(torch.int16).cpu().numpy().view(np.uint16)
+    y_all = y.cpu().numpy()
+    rows, cols = [], []
+    for e in range(E):
+        n_e = int(offsets[e + 1] - offsets[e])
+        blk = 192 if n_e >= 64 else 16
+        for r0 in range(0, n_e, blk):
+            nr = min(blk, n_e - r0)
+            for c0 in range(0, H, 256):
+                rows.append(int(offsets[e]) + r0 + int(rng.integers(nr)))
+                cols.append(c0 + int(rng.integers(256)))
+    rows, cols = np.array(rows), np.array(cols)
+    experts = np.searchsorted(offsets, rows, side="right") - 1
+    worst = 0.0
+    for c0 in range(0, len(rows), 2048):
+        r, c, e = rows[c0:c0 + 2048], cols[c0:c0 + 2048], experts[c0:c0 + 2048]
+        W = omx.unpack(whost["w2_codes"][e, c], whost["w2_scales"][e, c])        # [n, I]
+        hv = omx.bf16_bits_to_f64(h_all[r])                                      # [n, I]
+        exact = (W * hv).sum(1)
+        mag = np.abs(W * hv).sum(1)
+        err = np.abs(y_all[r, c].astype(np.float64) - exact)
+        assert np.all(err <= 2.0 * I * 2.0 ** -24 * mag + 1e-30), "y element out of bound"
+        worst = max(worst, float((err / np.maximum(mag, 1e-300)).max()))
+    say("  %s: %d sampled y elements (one per down item), worst |d| / sum|h w| %.3g"
+        % (name, len(rows), worst))
+
+    # out: one element of every combine item (a token by 2048 columns),
+    # against the slot-ordered sum of the GPU's own y rows in float64
+    w_h = w_d.cpu().numpy().astype(np.float64)
+    p2r = lists["pair_to_row"].reshape(T, k)
+    out_all = out.cpu().numpy()
+    toks = np.repeat(np.arange(T), (H + 2047) // 2048)
+    cb = np.tile(np.arange(0, H, 2048), T)
+    cols = cb + rng.integers(0, np.minimum(2048, H - cb))
+    terms = w_h[toks] * y_all[p2r[toks], cols[:, None]].astype(np.float64)   # [n, k]
+    err = np.abs(out_all[toks, cols] - terms.sum(1))
+    assert np.all(err <= 2.0 * k * 2.0 ** -24 * np.abs(terms).sum(1) + 1e-30), \
+        "out element out of bound"
+    say("  %s: %d sampled out elements (one per combine item)" % (name, len(toks)))
