@@ -94,6 +94,10 @@ int mxfp4_pack(const void* x, int x_dtype, int64_t rows, int64_t K,
  * y = E2M1(code) * 2^(e-127), computed exactly and rounded to the output type
  * (exact for every finite result, subnormals included; f32 overflows to Inf
  * only for e >= 253).  A scale byte 0xFF gives a quiet NaN for the block.
+ * The pages store the experts in MXFP4 with block size 32
+ * ("MiMo-V2.5-Pro-FP4-DFlash" model card, §2 "FP4 Quantization"; nxbn.cn
+ * article, "量化策略的智能选择": store_dtype mxfp4, mxfp4_block_size 32); the
+ * element and scale encodings are OCP MX v1.0's E2M1 and E8M0 (reading).
  */
 int mxfp4_unpack(const uint8_t* codes, const uint8_t* scales, int64_t rows,
                  int64_t K, void* y, int y_dtype, void* stream);
@@ -223,10 +227,16 @@ int moe_route_permute(const float* logits, int T, int E, int k, int32_t* topk_id
  * For row r of expert e with token t = sorted_pairs[r] / k:
  *   g = W_gate,e x_t, u = W_up,e x_t (fp32 accumulation),
  *   h_r = bf16_rne(silu(g) * u), silu(g) = g / (1 + exp(-g)).
- * The SwiGLU form without biases is the reading of the expert FFN (the pages
- * say only that the experts are MXFP4 and the activations higher precision).
- * Scale bytes must lie in 0..254; byte 0 (2^-127) is taken as zero, a
- * difference of at most 6*2^-127 per weight.
+ * The pages fix MXFP4 experts with block 32 and higher-precision activations
+ * ("MiMo-V2.5-Pro-FP4-DFlash" model card, §2 "FP4 Quantization"; bf16 from
+ * §5 "Deployment", --dtype bfloat16) and 384 experts with 8 active per token
+ * (nxbn.cn article, "架构设计与配置详解"); the SwiGLU form without biases and
+ * the gate-then-up row order are readings (the pages do not describe the
+ * expert FFN).
+ * Scale bytes must lie in 1..254 (2^-126 .. 2^127).  Byte 0 (2^-127, below
+ * the normal fp32 range) is outside the contract: the kernels take it as
+ * zero, which differs from mxfp4_unpack by at most 6*2^-127 per weight; byte
+ * 255 (NaN) is outside it too.
  */
 int moe_mxfp4_gate_up_swiglu(const uint16_t* x_bf16, const int32_t* sorted_pairs,
                              const int32_t* offsets, int T, int H, int I, int E,
@@ -240,6 +250,11 @@ int moe_mxfp4_gate_up_swiglu(const uint16_t* x_bf16, const int32_t* sorted_pairs
  *   offsets    [E+1] from moe_permute, read
  *   w2_codes   [E, H, I/2] uint8, w2_scales [E, H, I/32] uint8, blocks along I
  *   y          [T*k, H] f32, written in sorted order: y_r = W_down,e h_r
+ *              (fp32 accumulation of the bf16 h and the exactly dequantised
+ *              weights)
+ * Same sources and readings as moe_mxfp4_gate_up_swiglu (model card §2 for
+ * the MXFP4 format and block size; the down projection completes the
+ * reading's SwiGLU FFN); scale bytes in 1..254 as there.
  */
 int moe_mxfp4_down(const uint16_t* h_bf16, const int32_t* offsets, int T, int H,
                    int I, int E, int k, const uint8_t* w2_codes,
@@ -253,16 +268,23 @@ int moe_mxfp4_down(const uint16_t* h_bf16, const int32_t* offsets, int T, int H,
  *   out         [T, H] f32, written: out_t = sum_{j=0..k-1} w_tj * y[row(t,j)],
  *               summed in slot order j (deterministic); a dropped pair
  *               (pair_to_row < 0) contributes nothing
+ * Not on the pages: they name the routed experts (8 of 384, nxbn.cn
+ * article, "架构设计与配置详解") but not how their outputs are mixed.  The
+ * reading is the routing-weighted sum with the weights of moe_route_topk, in
+ * fp32, with no shared expert and no routed scaling factor.
  */
 int moe_combine(const float* y, const float* topk_w, const int32_t* pair_to_row,
                 int T, int H, int k, float* out, void* stream);
 
 /*
- * moe_mxfp4_layer — the whole layer: enqueues exactly moe_route_topk,
- * moe_permute, moe_mxfp4_gate_up_swiglu, moe_mxfp4_down and moe_combine on
- * `stream`, with the caller's intermediate buffers (topk_ids [T,k],
- * topk_w [T,k], counts [E], offsets [E+1], sorted_pairs [T*k],
- * pair_to_row [T*k], h [T*k, I] bf16, y [T*k, H] f32).
+ * moe_mxfp4_layer — the whole layer: enqueues moe_route_permute (which
+ * runs routing and grouping as one fused launch for T <= 16, else as
+ * moe_route_topk then moe_permute), moe_mxfp4_gate_up_swiglu,
+ * moe_mxfp4_down and moe_combine on `stream`, with the caller's intermediate
+ * buffers (topk_ids [T,k], topk_w [T,k], counts [E], offsets [E+1],
+ * sorted_pairs [T*k], pair_to_row [T*k], h [T*k, I] bf16, y [T*k, H] f32)
+ * and grouping workspace (moe_permute_workspace_bytes).  Results are those of
+ * the separate calls, bit for bit.  Sources and readings: those of each call.
  */
 int moe_mxfp4_layer(const uint16_t* x_bf16, const float* logits, int T, int H,
                     int I, int E, int k, const uint8_t* w13_codes,
