@@ -12,8 +12,9 @@ Each workload runs --warmup steps, then more until --warm-seconds have passed
 (the clocks settle under sustained load), then three timed passes of --steps
 steps: the headline region (two events around all steps), per-step events
 (median / p10 / p90) and events around every entry point (per-kernel times).
-The verify_t8 run then times verify_t64, zipf_t512 and prefill_t8192 on the
-same weights with the same flags.
+The verify_t8 run also times the same step through the persistent decode
+layer entry point (one kernel), then verify_t64, zipf_t512 and prefill_t8192
+on the same weights with the same flags.
 
 Prints ONE JSON line on stdout; diagnostics go to stderr.
   value         tokens/s of the whole layer (headline region)
@@ -561,6 +562,56 @@ def time_layer(run, steps, warmup, warm_s, clocks=None):
     return res
 
 
+def time_decode_layer(run, steps, warmup, warm_s):
+    """The same workload through moe_mxfp4_decode_layer (the whole layer as
+    one persistent kernel), timed like time_layer's first two passes; None
+    when that entry point does not take the sizes."""
+    torch, mm, cfg, b = run.torch, run.mm, run.cfg, run.b
+    ws = mm.decode_layer_workspace(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, b.out.device)
+    if ws is None:
+        return None
+
+    def step():
+        w = run.wsets[run.n & 1]
+        run.n += 1
+        mm.moe_mxfp4_decode_layer(run.x, run.logits, cfg.k, w["w13_codes"], w["w13_scales"],
+                                  w["w2_codes"], w["w2_scales"], ws, buffers=b)
+    Ev = lambda: torch.cuda.Event(enable_timing=True)       # noqa: E731
+    torch.cuda._sleep(1000)      # marks the start of this phase in a kernel trace
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0, batch = time.perf_counter(), 1
+    while time.perf_counter() - t0 < warm_s:
+        for _ in range(batch):
+            step()
+        torch.cuda.synchronize()
+        batch = min(2 * batch, 512)
+    s = run.stream
+    e0, e1 = Ev(), Ev()
+    e0.record(s)
+    for _ in range(steps):
+        step()
+    e1.record(s)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    evs = [Ev() for _ in range(steps + 1)]
+    evs[0].record(s)
+    for i in range(steps):
+        step()
+        evs[i + 1].record(s)
+    torch.cuda.synchronize()
+    per = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(steps)])
+    err = int(ws.view(torch.int32)[2].item())
+    log("%s decode layer (one persistent kernel): %.4f ms/step, median %.4f, error word %d"
+        % (cfg.name, ms, np.median(per), err))
+    return {"entry": "moe_mxfp4_decode_layer", "ms_per_step": round(ms, 5),
+            "ms_per_step_p10": round(float(np.percentile(per, 10)), 5),
+            "ms_per_step_median": round(float(np.median(per)), 5),
+            "ms_per_step_p90": round(float(np.percentile(per, 90)), 5),
+            "tokens_per_s": round(cfg.T / (ms * 1e-3), 1), "error_word": err}
+
+
 def layer_figures(cfg, counts, res):
     """Rates of one timed workload: tokens/s, effective weight bandwidth,
     fractions of the HBM and bf16 MFMA peaks, and the same for each
@@ -721,6 +772,11 @@ def main():
     if args.save_counts:
         np.save(args.save_counts, counts)
     fig = layer_figures(cfg, counts, res)
+    fused = time_decode_layer(run, steps, warmup, args.warm_seconds)
+    if fused is not None:
+        fused["hbm_frac_layer"] = round(fig["weight_bytes_touched"] / (fused["ms_per_step"] * 1e-3)
+                                        / 1e9 / HBM_PEAK_GBPS, 4)
+        fused["vs_multi_launch"] = round(fig["ms_per_step"] / fused["ms_per_step"], 4)
 
     cpu = None
     if args.cpu_budget > 0:
@@ -770,6 +826,7 @@ def main():
         "warmup_s": round(res["warmup_s"], 2),
         "roofline": roofline,
         "down": fig["down"],
+        "decode_layer": fused,
         "workloads": extra,
         "clocks": clocks.summary(),
         "host_cpu": host_cpu_model(),

@@ -294,6 +294,42 @@ int moe_mxfp4_layer(const uint16_t* x_bf16, const float* logits, int T, int H,
                     int32_t* pair_to_row, uint16_t* h_bf16, float* y, float* out,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* Workspace moe_mxfp4_decode_layer needs for these sizes (0 when the
+ * persistent kernel does not take them). */
+size_t moe_mxfp4_decode_layer_workspace_bytes(int T, int H, int I, int E, int k);
+
+/*
+ * moe_mxfp4_decode_layer — the whole layer for a verify-sized batch as ONE
+ * persistent kernel: routing, grouping, gate/up + SwiGLU, down and combine.
+ *   arguments and results as moe_mxfp4_layer (results equal bit for bit),
+ *   except the workspace:
+ *   workspace  moe_mxfp4_decode_layer_workspace_bytes(...) bytes, 16-byte
+ *              aligned, ZERO-FILLED by the caller before its first use; every
+ *              call leaves it zero-filled for the next one, except 32-bit word
+ *              2, which becomes nonzero (and stays so) if one of the kernel's
+ *              bounded waits gave up, in which case the call's outputs are not
+ *              valid.  Calls sharing a workspace must not overlap.
+ * Taken shapes: 1 <= T <= 16, T*k <= 512, H and I multiples of 2048 up to
+ * 8192, E <= 1024; other shapes return MXM_ERR_UNIMPLEMENTED (use
+ * moe_mxfp4_layer).  The pages credit the decode speed of the serving
+ * runtime to a persistent engine kernel that removes the gaps at operator
+ * boundaries ("Xiaomi MiMo-V2.5-Pro-UltraSpeed" release notes, "TileRT
+ * 執行模型", item 1); the verify block of 8 tokens per sequence is the
+ * model card's §3 DFlash.  One workgroup per CU; each routes every token
+ * itself, takes gate/up units from a queue in tile order, then down units
+ * from a second queue once their tile's gate/up units are in, and the
+ * workgroup that completes a column block combines it.  Every wait is for
+ * units already claimed by running workgroups that never wait, so the grid
+ * need not be resident all at once.  Errors as moe_mxfp4_layer.
+ */
+int moe_mxfp4_decode_layer(const uint16_t* x_bf16, const float* logits, int T, int H,
+                           int I, int E, int k, const uint8_t* w13_codes,
+                           const uint8_t* w13_scales, const uint8_t* w2_codes,
+                           const uint8_t* w2_scales, int32_t* topk_ids, float* topk_w,
+                           int32_t* counts, int32_t* offsets, int32_t* sorted_pairs,
+                           int32_t* pair_to_row, uint16_t* h_bf16, float* y, float* out,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
 /*
  * moe_mxfp4_layer_noalloc — moe_mxfp4_layer for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops,

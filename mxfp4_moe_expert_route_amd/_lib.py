@@ -31,6 +31,10 @@ SIGNATURES = {
     "moe_mxfp4_down": (_c_int, [_p, _p, _c_int, _c_int, _c_int, _c_int, _c_int, _p, _p, _p, _p]),
     "moe_combine": (_c_int, [_p, _p, _p, _c_int, _c_int, _c_int, _p, _p]),
     "mxm_stream_xor": (_c_int, [_p, _c_i64, _c_int, _p, _p]),
+    "moe_mxfp4_decode_layer_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int]),
+    "moe_mxfp4_decode_layer": (_c_int, [_p, _p, _c_int, _c_int, _c_int, _c_int, _c_int, _p, _p,
+                                        _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _c_size,
+                                        _p]),
     "moe_mxfp4_layer_noalloc": (_c_int, [_p, _p, _c_int, _c_int, _c_int, _c_int, _c_int, _p, _p,
                                          _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p]),
     "moe_mxfp4_layer": (_c_int, [_p, _p, _c_int, _c_int, _c_int, _c_int, _c_int, _p, _p, _p, _p,

@@ -346,6 +346,36 @@ int moe_mxfp4_layer(const uint16_t* x_bf16, const float* logits, int T, int H, i
   return moe_combine(y, topk_w, pair_to_row, T, H, k, out, stream);
 }
 
+size_t moe_mxfp4_decode_layer_workspace_bytes(int T, int H, int I, int E, int k) {
+  if (check_ffn_shape(T, H, I, E, k) != MXM_OK || !mxm::decode_layer_supported(T, H, I, E, k))
+    return 0;
+  return mxm::decode_layer_workspace_bytes();
+}
+
+int moe_mxfp4_decode_layer(const uint16_t* x_bf16, const float* logits, int T, int H, int I,
+                           int E, int k, const uint8_t* w13_codes, const uint8_t* w13_scales,
+                           const uint8_t* w2_codes, const uint8_t* w2_scales, int32_t* topk_ids,
+                           float* topk_w, int32_t* counts, int32_t* offsets,
+                           int32_t* sorted_pairs, int32_t* pair_to_row, uint16_t* h_bf16,
+                           float* y, float* out, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  int st = check_ffn_shape(T, H, I, E, k);
+  if (st != MXM_OK) return st;
+  if (T == 0) return MXM_OK;
+  if (!mxm::decode_layer_supported(T, H, I, E, k)) return MXM_ERR_UNIMPLEMENTED;
+  if (workspace_bytes < mxm::decode_layer_workspace_bytes()) return MXM_ERR_WORKSPACE;
+  if ((st = check_layer_pointers(x_bf16, logits, w13_codes, w13_scales, w2_codes, w2_scales,
+                                 topk_ids, topk_w, counts, offsets, sorted_pairs, pair_to_row,
+                                 h_bf16, y, out)) != MXM_OK)
+    return st;
+  if (!workspace) return MXM_ERR_NULL;
+  if (!aligned(workspace, 16)) return MXM_ERR_ALIGN;
+  return launched(mxm::launch_decode_layer(x_bf16, logits, T, H, I, E, k, w13_codes, w13_scales,
+                                           w2_codes, w2_scales, topk_ids, topk_w, counts, offsets,
+                                           sorted_pairs, pair_to_row, h_bf16, y, out, workspace,
+                                           as_stream(stream)));
+}
+
 int moe_mxfp4_layer_noalloc(const uint16_t* x_bf16, const float* logits, int T, int H, int I,
                             int E, int k, const uint8_t* w13_codes, const uint8_t* w13_scales,
                             const uint8_t* w2_codes, const uint8_t* w2_scales, int32_t* topk_ids,

@@ -168,6 +168,17 @@ hipError_t launch_gate_up_dense(const uint16_t* x, const int32_t* sorted_pairs,
 hipError_t launch_down_dense(const uint16_t* h, const int32_t* offsets, int T, int H, int I,
                              int E, int k, const uint8_t* codes, const uint8_t* scales, float* y,
                              hipStream_t s);
+// Persistent fused decode layer (routing, grouping, gate/up, down, combine in
+// one cooperative launch) for T <= 16; its workspace is zero-filled by the
+// caller before the first call and left zero-filled.
+bool decode_layer_supported(int T, int H, int I, int E, int k);
+size_t decode_layer_workspace_bytes();
+hipError_t launch_decode_layer(const uint16_t* x, const float* logits, int T, int H, int I, int E,
+                               int k, const uint8_t* w13c, const uint8_t* w13s,
+                               const uint8_t* w2c, const uint8_t* w2s, int32_t* ids, float* w,
+                               int32_t* counts, int32_t* offsets, int32_t* sorted_pairs,
+                               int32_t* pair_to_row, uint16_t* h, float* y, float* out,
+                               void* workspace, hipStream_t s);
 // Rejection-sampling verification of drafted blocks.
 size_t verify_workspace_bytes(int B, int L);
 hipError_t launch_verify(const float* target, const float* draft, const int32_t* tokens,

@@ -26,18 +26,23 @@ __global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ lo
 }
 
 // Small batches (T <= 16): routing and grouping in one workgroup of 16 waves.
-// Wave t routes token t; the ids go to global memory and to LDS, and after
-// one barrier the workgroup groups the pairs from LDS.  Same functions as the
-// two separate kernels, so the same results; one launch and one round trip
-// to memory fewer.
+// Wave t routes token t; the ids go to global memory and to LDS, and each
+// chosen expert's token mask gets bit t.  After one barrier the workgroup
+// groups the pairs from the masks (group_small).  Same routing function as
+// k_route_topk and the same lists as k_permute, bit for bit; one launch and
+// one round trip to memory fewer.
 template <int NPER>
 __global__ __launch_bounds__(kFusedWaves * kWave) void k_route_permute(
     const float* __restrict__ logits, int T, int E, int k, int32_t* __restrict__ ids,
     float* __restrict__ w, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ pair_to_row) {
-  extern __shared__ int32_t smem[];            // permutation tables, then the ids
+  extern __shared__ int32_t smem[];            // mask [E], offsets [E + 1], ids [T k]
   __shared__ int32_t wave_sum[kFusedWaves];
-  int32_t* lds_ids = smem + (kFusedWaves + 1) * E;
+  uint32_t* mask = reinterpret_cast<uint32_t*>(smem);
+  int32_t* off_lds = smem + E;
+  int32_t* lds_ids = smem + 2 * E + 1;
+  for (int e = threadIdx.x; e < E; e += kFusedWaves * kWave) mask[e] = 0u;
+  __syncthreads();
   const int t = threadIdx.x >> 6;
   const int lane = lane_id();
   if (t < T) {
@@ -48,18 +53,19 @@ __global__ __launch_bounds__(kFusedWaves * kWave) void k_route_permute(
       ids[int64_t(t) * k + lane] = my_id;
       w[int64_t(t) * k + lane] = my_w;
       lds_ids[t * k + lane] = my_id;
+      atomicOr(&mask[my_id], 1u << t);
     }
   }
   __syncthreads();
-  permute_block<kFusedWaves>(lds_ids, 0, T * k, E, nullptr, counts, offsets, sorted_pairs,
-                             pair_to_row, smem, wave_sum);
+  group_small<kFusedWaves>(lds_ids, mask, T * k, E, k, counts, offsets, off_lds, sorted_pairs,
+                           pair_to_row, nullptr, nullptr, wave_sum);
 }
 
 template <int NPER>
 hipError_t launch_fused_n(const float* logits, int T, int E, int k, int32_t* ids, float* w,
                           int32_t* counts, int32_t* offsets, int32_t* sorted_pairs,
                           int32_t* pair_to_row, hipStream_t s) {
-  const size_t lds = (size_t(kFusedWaves + 1) * E + size_t(T) * k) * sizeof(int32_t);
+  const size_t lds = (size_t(2) * E + 1 + size_t(T) * k) * sizeof(int32_t);
   k_route_permute<NPER><<<1, kFusedWaves * kWave, lds, s>>>(logits, T, E, k, ids, w, counts,
                                                             offsets, sorted_pairs, pair_to_row);
   return hipGetLastError();
@@ -278,7 +284,7 @@ hipError_t launch_router_logits(const uint16_t* x, const float* w_router, const 
 
 bool route_permute_fusable(int T, int E, int k) {
   return T >= 1 && T <= kFusedWaves &&
-         (size_t(kFusedWaves + 1) * E + size_t(T) * k) * sizeof(int32_t) <= 64 * 1024;
+         (size_t(2) * E + 1 + size_t(T) * k) * sizeof(int32_t) <= 64 * 1024;
 }
 
 hipError_t launch_route_permute(const float* logits, int T, int E, int k, int32_t* ids, float* w,

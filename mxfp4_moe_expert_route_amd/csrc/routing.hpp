@@ -240,5 +240,76 @@ __device__ __forceinline__ void permute_block(const int32_t* ids, int r0, int r1
   }
 }
 
+// Grouping for small batches (T <= 32 tokens), by a whole workgroup of NW
+// waves.  A token never picks an expert twice, so expert e's pairs are fixed
+// by the set of tokens that chose it: mask[e] has bit t set when token t did
+// (the caller clears it, sets the bits from its routing lanes, then
+// barriers).  Then, for pair p = t k + j with expert e:
+//   counts[e]  = popcount(mask[e])
+//   offsets[e] = sum of the counts of experts below e (one block scan)
+//   row        = offsets[e] + popcount(mask[e] & (2^t - 1)),
+// which is the stable order by p within the expert, so the lists are those
+// of permute_block bit for bit.  The same scan numbers the touched experts:
+// when `tiles` is set, tile i (the i-th expert with pairs, in expert order)
+// gets {e | count << 16, offsets[e]} and *ntiles the number of tiles.  ids
+// [R] and mask [E] are in LDS; off_lds is an LDS copy of offsets [E + 1]; the
+// other outputs may be global or LDS.
+template <int NW>
+__device__ __forceinline__ void group_small(const int32_t* ids, const uint32_t* mask, int R,
+                                            int E, int k, int32_t* counts, int32_t* offsets,
+                                            int32_t* off_lds, int32_t* sorted_pairs,
+                                            int32_t* pair_to_row, int2* tiles, int* ntiles,
+                                            int32_t* wave_sum) {
+  constexpr int NT = NW * kWave;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = lane_id();
+  const int ept = (E + NT - 1) / NT;              // experts per thread, consecutive
+  const int e0 = tid * ept;
+  // count (bits 0..15) and touched flag (bits 16..31) of each expert, summed:
+  // R <= 32 * 32 pairs and E <= 1024 experts fit their halves
+  int local = 0;
+  for (int i = 0; i < ept; ++i) {
+    const int e = e0 + i;
+    if (e < E) {
+      const int c = __popc(mask[e]);
+      local += c | ((c > 0) << 16);
+    }
+  }
+  const int incl = wave_incl_scan(local);
+  if (lane == kWave - 1) wave_sum[wave] = incl;
+  __syncthreads();
+  int run = incl - local, total = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int v = wave_sum[w];
+    run += w < wave ? v : 0;
+    total += v;
+  }
+  for (int i = 0; i < ept; ++i) {
+    const int e = e0 + i;
+    if (e >= E) break;
+    const int c = __popc(mask[e]);
+    const int off = run & 0xffff;
+    counts[e] = c;
+    offsets[e] = off;
+    off_lds[e] = off;
+    if (tiles && c > 0) tiles[run >> 16] = make_int2(e | (c << 16), off);
+    run += c | ((c > 0) << 16);
+  }
+  if (tid == 0) {
+    offsets[E] = total & 0xffff;
+    off_lds[E] = total & 0xffff;
+    if (ntiles) *ntiles = total >> 16;
+  }
+  __syncthreads();
+  for (int p = tid; p < R; p += NT) {
+    const int t = p / k, e = ids[p];
+    const int row = off_lds[e] + __popc(mask[e] & ((1u << t) - 1u));
+    sorted_pairs[row] = p;
+    pair_to_row[p] = row;
+  }
+}
+
 }  // namespace
 }  // namespace mxm

@@ -272,6 +272,48 @@ def moe_mxfp4_layer(x, logits, k, w13_codes, w13_scales, w2_codes, w2_scales, bu
     return b
 
 
+def moe_mxfp4_decode_layer_workspace_bytes(T, H, I, E, k):
+    """Bytes of the zero-filled workspace moe_mxfp4_decode_layer needs (0: the
+    persistent kernel does not take these sizes)."""
+    return int(lib().moe_mxfp4_decode_layer_workspace_bytes(T, H, I, E, k))
+
+
+def decode_layer_workspace(T, H, I, E, k, device):
+    """A zero-filled workspace for moe_mxfp4_decode_layer (None if the sizes
+    are not taken).  Each call leaves it zero-filled, so it is reusable."""
+    n = moe_mxfp4_decode_layer_workspace_bytes(T, H, I, E, k)
+    return torch.zeros(n, dtype=torch.uint8, device=device) if n else None
+
+
+def moe_mxfp4_decode_layer(x, logits, k, w13_codes, w13_scales, w2_codes, w2_scales, workspace,
+                           buffers=None):
+    """The whole layer as one persistent kernel (verify-sized batches, T <= 16).
+
+    `workspace` comes from decode_layer_workspace (zero-filled; the call leaves
+    it so).  Returns the LayerBuffers holding every intermediate; `.out` is the
+    result, equal bit for bit to moe_mxfp4_layer's."""
+    _need(x, "x", torch.bfloat16)
+    T, H = x.shape
+    E, two_i, _ = w13_codes.shape
+    I = two_i // 2
+    dev = x.device
+    _need(logits, "logits", torch.float32, (T, E), dev)
+    _need(w13_codes, "w13_codes", torch.uint8, (E, 2 * I, H // 2), dev)
+    _need(w13_scales, "w13_scales", torch.uint8, (E, 2 * I, H // 32), dev)
+    _need(w2_codes, "w2_codes", torch.uint8, (E, H, I // 2), dev)
+    _need(w2_scales, "w2_scales", torch.uint8, (E, H, I // 32), dev)
+    _need(workspace, "workspace", torch.uint8, None, dev)
+    b = buffers if buffers is not None else LayerBuffers(T, H, I, E, k, dev)
+    if (b.T, b.H, b.I, b.E, b.k) != (T, H, I, E, k):
+        raise ValueError("buffers were made for another shape")
+    check(lib().moe_mxfp4_decode_layer(
+        _ptr(x), _ptr(logits), T, H, I, E, k, _ptr(w13_codes), _ptr(w13_scales), _ptr(w2_codes),
+        _ptr(w2_scales), _ptr(b.topk_ids), _ptr(b.topk_w), _ptr(b.counts), _ptr(b.offsets),
+        _ptr(b.sorted_pairs), _ptr(b.pair_to_row), _ptr(b.h), _ptr(b.y), _ptr(b.out),
+        _ptr(workspace), workspace.numel(), _stream()), "moe_mxfp4_decode_layer")
+    return b
+
+
 def moe_mxfp4_layer_noalloc(x, logits, k, w13_codes, w13_scales, w2_codes, w2_scales, buffers):
     """moe_mxfp4_layer through the entry point that allocates nothing: its
     grouping workspace is the library's fixed device scratch (the workspace

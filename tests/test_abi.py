@@ -33,6 +33,7 @@ def test_header_declares_the_boundary():
               "dflash_verify_accept", "dflash_verify_workspace_bytes", "moe_permute",
               "moe_permute_workspace_bytes", "moe_route_permute", "moe_mxfp4_gate_up_swiglu", "moe_mxfp4_down",
               "moe_combine", "moe_mxfp4_layer", "moe_mxfp4_layer_noalloc", "mxm_stream_xor",
+              "moe_mxfp4_decode_layer", "moe_mxfp4_decode_layer_workspace_bytes",
               "mxm_status_string", "mxm_version"):
         assert n in names
 
@@ -162,3 +163,22 @@ def test_noalloc_layer_argument_checks(lib):
     assert f(P + 4, P, 8, 6144, 2048, 384, 8, *ptrs, None) == -4            # misaligned x
     # nulls are caught before the scratch is looked up, also above 8192 pairs
     assert f(None, P, 2048, 256, 128, 384, 8, *ptrs, None) == -1
+
+
+def test_decode_layer_argument_checks(lib):
+    nbytes = lib.moe_mxfp4_decode_layer_workspace_bytes
+    f = lib.moe_mxfp4_decode_layer
+    ws = nbytes(8, 6144, 2048, 384, 8)
+    assert ws >= 2048
+    assert nbytes(17, 6144, 2048, 384, 8) == 0          # more than 16 tokens
+    assert nbytes(8, 6144, 1024, 384, 8) == 0           # I not a multiple of 2048
+    assert nbytes(8, 16384, 2048, 384, 8) == 0          # H above 8192
+    assert nbytes(16, 2048, 2048, 1024, 32) == ws       # T k = 512, the most it takes
+    ptrs = [P] * 13
+    assert f(P, P, 0, 6144, 2048, 384, 8, *ptrs, P, ws, None) == 0         # empty: no-op
+    assert f(P, P, 17, 6144, 2048, 384, 8, *ptrs, P, ws, None) == -6       # not taken
+    assert f(P, P, 8, 6144, 2048, 384, 8, *ptrs, P, ws - 1, None) == -7    # workspace
+    assert f(P, P, 8, 6144, 2048, 384, 8, *ptrs, None, ws, None) == -1     # null workspace
+    assert f(P, P, 8, 6144, 2048, 384, 8, *ptrs, P + 8, ws, None) == -4    # misaligned
+    assert f(None, P, 8, 6144, 2048, 384, 8, *ptrs, P, ws, None) == -1     # null x
+    assert f(P, P, 8, 6144, 2048, 384, 40, *ptrs, P, ws, None) == -2       # k > 32
