@@ -20,8 +20,8 @@ Prints ONE JSON line on stdout; diagnostics go to stderr.
   value         tokens/s of the whole layer (headline region)
   roofline      the gate/up contraction (the kernel that streams 2/3 of the
                 weight bytes): algorithmic bytes per launch / its mean duration
-                from HIP events around its calls, against 8 TB/s (or the bf16
-                MFMA peak where it is compute-bound)
+                from HIP events just before and after its calls, against 8 TB/s
+                (or the bf16 MFMA peak where it is compute-bound)
   workloads     the same figures for the other page-shaped workloads
   cpu_baseline  the float64 CPU oracle on a bounded sample of the same tokens
 """
@@ -55,18 +55,23 @@ def log(*a):
 ENTRY_KERNELS = {
     "moe_mxfp4_gate_up_swiglu": ("k_decode<true>", "k_gate_up<", "k_dense<true>"),
     "moe_mxfp4_down": ("k_decode<false>", "k_down<", "k_dense<false>"),
+    "moe_mxfp4_decode_layer": ("k_decode_layer",),
 }
-# source file of each kernel family; every measurement also depends on the
+# source files of each kernel family; every measurement also depends on the
 # shared helpers and on the host code that picks the kernel
-KERNEL_FILES = {"k_decode": "expert_decode.hip", "k_gate_up": "expert_stream.hip",
-                "k_down": "expert_stream.hip", "k_dense": "expert_dense.hip"}
+KERNEL_FILES = {"k_decode<": ("expert_decode.hip", "decode_stream.hpp"),
+                "k_decode_layer": ("decode_layer.hip", "decode_stream.hpp", "routing.hpp"),
+                "k_gate_up": ("expert_stream.hip",), "k_down": ("expert_stream.hip",),
+                "k_dense": ("expert_dense.hip",)}
 COMMON_FILES = ("common.hpp", "expert_stream.hip", "api.hip")
 
 
 def kernel_sources(kernel_names):
     files = set(COMMON_FILES)
     for n in kernel_names:
-        files.update(f for k, f in KERNEL_FILES.items() if k in n)
+        for k, fs in KERNEL_FILES.items():
+            if k in n:
+                files.update(fs)
     return sorted(files)
 
 
@@ -137,7 +142,9 @@ def _algorithmic_bytes(cfg, counts):
     touched = int((np.asarray(counts) > 0).sum())
     w13 = 2 * I * H // 2 + 2 * I * H // 32
     w2 = H * I // 2 + H * I // 32
-    return {"moe_mxfp4_gate_up_swiglu": touched * w13 + T * H * 2,
+    return {"moe_mxfp4_decode_layer": touched * (w13 + w2) + T * H * 2 + T * cfg.E * 4
+            + T * H * 4,
+            "moe_mxfp4_gate_up_swiglu": touched * w13 + T * H * 2,
             "moe_mxfp4_down": touched * w2, "touched": touched}
 
 
@@ -150,7 +157,7 @@ def _is_phase_marker(name):
     return "spin_kernel" in name or "sleep" in name.lower()
 
 
-def trace_tables(trace_dir, phases):
+def trace_tables(trace_dir, phases, show=None):
     """Per-workload kernel statistics from a rocprofv3 kernel trace of one
     bench.py run: the dispatches are cut at the marker kernel that starts
     each workload, in the order `phases` names them."""
@@ -168,6 +175,8 @@ def trace_tables(trace_dir, phases):
         per.setdefault(phases[seg], {}).setdefault(_short_kernel_name(name), []).append(dur)
     out = []
     for ph in phases:
+        if show and ph not in show:
+            continue
         ks = per.get(ph, {})
         tot = sum(sum(v) for v in ks.values()) or 1.0
         out += ["Workload %s (every dispatch of the workload: warm-up and timed passes):" % ph, "",
@@ -177,6 +186,47 @@ def trace_tables(trace_dir, phases):
             out.append("| %s | %d | %.1f | %.1f | %.1f | %.1f | %.1f%% |" % (
                 n, len(v), np.mean(v), np.median(v), min(v), max(v), 100.0 * sum(v) / tot))
         out.append("")
+    return out
+
+
+def mfma_table(d, cfg, counts):
+    """Matrix-core counters of the dense contractions from one rocprofv3 --pmc
+    run: SQ_VALU_MFMA_BUSY_CYCLES (summed over the SIMDs), GRBM_GUI_ACTIVE
+    (the dispatch's GPU cycles, summed over the XCDs) and
+    SQ_INSTS_VALU_MFMA_MOPS_BF16 (bf16 MFMA work in units of 512 flops).
+    Busy = busy cycles / (active cycles per XCD x SIMDs): the share of the
+    kernel's own cycles the matrix units worked, at whatever clock it ran;
+    clock = active cycles per XCD / the dispatch's duration."""
+    agent = [r for r in _csv_rows(_find_csv(d, "agent_info.csv")) if int(r.get("Simd_Count") or 0) > 0]
+    nxcc = int(agent[0]["Num_Xcc"]) if agent else 8
+    nsimd = int(agent[0]["Simd_Count"]) if agent else 1024
+    rows = _csv_rows(_find_csv(d, "counter_collection.csv"))
+    per = {}
+    for r in rows:
+        n = _short_kernel_name(r["Kernel_Name"])
+        if "k_dense" not in n:
+            continue
+        v = per.setdefault(n, {}).setdefault(r["Dispatch_Id"], {})
+        v[r["Counter_Name"]] = float(r["Counter_Value"])
+        v["ns"] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+    out = ["Matrix-core counters (rocprofv3 --pmc, %d XCDs, %d SIMDs; per dispatch, averaged):"
+           % (nxcc, nsimd), "",
+           "| kernel | dispatches | MFMA busy share of the kernel's cycles | clock (GHz) | "
+           "busy x clock / 2.4 GHz | bf16 MFMA flops (counter) | flops of all rows (4 or 2 T k H I) |",
+           "|---|---|---|---|---|---|---|"]
+    R = cfg.T * cfg.k
+    for n, disp in sorted(per.items()):
+        vs = [v for v in disp.values() if "SQ_VALU_MFMA_BUSY_CYCLES" in v and v.get("GRBM_GUI_ACTIVE")]
+        busy = np.mean([v["SQ_VALU_MFMA_BUSY_CYCLES"] / (v["GRBM_GUI_ACTIVE"] / nxcc * nsimd)
+                        for v in vs])
+        clk = np.mean([v["GRBM_GUI_ACTIVE"] / nxcc / v["ns"] for v in vs])
+        flops = np.mean([v["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512.0 for v in disp.values()
+                         if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in v])
+        alg = (4.0 if "true" in n else 2.0) * R * cfg.H * cfg.I
+        out.append("| %s | %d | %.3f | %.2f | %.3f | %.4g | %.4g |"
+                   % (n, len(disp), busy, clk, busy * clk / 2.4, flops, alg))
+    out += ["", "The counted flops exceed those of the rows by the padding of each expert's last "
+            "16-row token subtile.", ""]
     return out
 
 
@@ -196,7 +246,8 @@ def summarize_profiles(args):
         out += ["Command (from /tmp, `TMPDIR=/tmp`, on one MI355X):", "", "```",
                 args.command, "```", ""]
     if args.trace_dir:
-        out += trace_tables(args.trace_dir, (args.phases or cfg.name).split(","))
+        out += trace_tables(args.trace_dir, (args.phases or cfg.name).split(","),
+                            args.show.split(",") if args.show else None)
     if args.stats_dir:
         rows = _csv_rows(_find_csv(args.stats_dir, "kernel_stats.csv"))
         out += ["| kernel | calls | average (us) | min (us) | max (us) | share |",
@@ -208,6 +259,8 @@ def summarize_profiles(args):
                 name, r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
                 float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
         out.append("")
+    if args.mfma_dir:
+        out += mfma_table(args.mfma_dir, cfg, np.load(args.counts) if args.counts else None)
     if args.fetch_dir and args.write_dir:
         known = cfg.E * 2 * cfg.I * cfg.H // 2          # the w13 codes clone
         per = {}
@@ -225,6 +278,8 @@ def summarize_profiles(args):
                     if any(p in r["Kernel_Name"] for p in pats):
                         by_kernel.setdefault(r["Kernel_Name"], []).append(
                             float(r["Counter_Value"]))
+                if not by_kernel:
+                    continue
                 names.setdefault(entry, set()).update(by_kernel)
                 per.setdefault(entry, {})[ctr] = sum(
                     np.mean(v) * 1024.0 * factors[ctr] for v in by_kernel.values())
@@ -246,7 +301,7 @@ def summarize_profiles(args):
             srcs = kernel_sources(names[entry])
             db["%s@%s" % (entry, cfg.name)] = {
                 "sources": srcs, "source_hash": kernel_source_hash(srcs),
-                "bytes_per_launch": int(round(tot)),
+                "bytes_per_launch": int(round(v["FETCH_SIZE"])) + int(round(v["WRITE_SIZE"])),
                 "fetch_bytes": int(round(v["FETCH_SIZE"])),
                 "write_bytes": int(round(v["WRITE_SIZE"])),
                 "algorithmic_bytes": int(alg[entry]),
@@ -476,33 +531,37 @@ class LayerRun:
         self.stream = torch.cuda.current_stream()
         self.n = 0                                  # steps run (for the weight copy parity)
 
-    def step(self, ev=None):
+    def step(self, ev=None, at=(0, 1, 2, 3, 4)):
+        """One layer step; ev[i] is recorded at point i (0: before routing, 1:
+        before gate/up, 2: before down, 3: before combine, 4: after) for the
+        points listed in `at`."""
         mm, b, k = self.mm, self.b, self.cfg.k
         w = self.wsets[self.n & 1]
         self.n += 1
-        if ev is not None:
-            ev[0].record(self.stream)
+
+        def mark(i):
+            if ev is not None and i in at:
+                ev[i].record(self.stream)
+        mark(0)
         mm.moe_route_permute(self.logits, k, b.topk_ids, b.topk_w, b.counts, b.offsets,
                              b.sorted_pairs, b.pair_to_row, b.workspace)
-        if ev is not None:
-            ev[1].record(self.stream)
+        mark(1)
         mm.moe_mxfp4_gate_up_swiglu(self.x, b.sorted_pairs, b.offsets, k, w["w13_codes"],
                                     w["w13_scales"], b.h)
-        if ev is not None:
-            ev[2].record(self.stream)
+        mark(2)
         mm.moe_mxfp4_down(b.h, b.offsets, k, w["w2_codes"], w["w2_scales"], b.y)
-        if ev is not None:
-            ev[3].record(self.stream)
+        mark(3)
         mm.moe_combine(b.y, b.topk_w, b.pair_to_row, b.out)
-        if ev is not None:
-            ev[4].record(self.stream)
+        mark(4)
 
 
 def time_layer(run, steps, warmup, warm_s, clocks=None):
-    """Warm up, then three passes of `steps` steps each:
+    """Warm up, then four passes of `steps` steps each:
       1. the headline region: two events around all steps, nothing inside;
       2. per-step times: one event between consecutive steps;
-      3. per-entry-point times: events around each call of every step.
+      3. per-entry-point times: events around each call of every step;
+      4. each contraction alone: events just before and after its call (fewer
+         markers between the kernels, for the roofline's launch times).
     Warm-up is `warmup` steps and then more until `warm_s` seconds have passed
     (the clocks settle under sustained load)."""
     torch = run.torch
@@ -551,14 +610,23 @@ def time_layer(run, steps, warmup, warm_s, clocks=None):
     parts = ("route_permute", "gate_up", "down", "combine")
     per_kernel = {p: np.array([kev[i][j].elapsed_time(kev[i][j + 1]) for i in range(steps)])
                   for j, p in enumerate(parts)}
+    alone = {}
+    for j, p in ((1, "gate_up"), (2, "down")):
+        aev = [[Ev() for _ in range(5)] for _ in range(steps)]
+        for i in range(steps):
+            run.step(aev[i], at=(j, j + 1))
+        torch.cuda.synchronize()
+        alone[p] = np.array([aev[i][j].elapsed_time(aev[i][j + 1]) for i in range(steps)])
     res = {"ms_per_step": ms_step, "wall_ms_per_step": wall * 1e3 / steps,
-           "per_step": per_step, "per_kernel": per_kernel, "warmup_steps": nwarm,
+           "per_step": per_step, "per_kernel": per_kernel, "alone": alone,
+           "warmup_steps": nwarm,
            "warmup_s": warm_elapsed}
     log("%s: events %.4f ms/step (wall %.4f), per-step median %.4f p10 %.4f p90 %.4f; "
         "warm-up %d steps in %.2f s" % (run.cfg.name, ms_step, res["wall_ms_per_step"],
                                        np.median(per_step), np.percentile(per_step, 10),
                                        np.percentile(per_step, 90), nwarm, warm_elapsed))
-    log("  " + ", ".join("%s %.1f us" % (p, np.median(v) * 1e3) for p, v in per_kernel.items()))
+    log("  " + ", ".join("%s %.1f us" % (p, np.median(v) * 1e3) for p, v in per_kernel.items())
+        + "; alone: " + ", ".join("%s %.1f us" % (p, np.mean(v) * 1e3) for p, v in alone.items()))
     return res
 
 
@@ -637,7 +705,7 @@ def layer_figures(cfg, counts, res):
                                     BF16_MFMA_PEAK_TFLOPS, 4)}
     for entry, part, fl in (("moe_mxfp4_gate_up_swiglu", "gate_up", 4.0),
                             ("moe_mxfp4_down", "down", 2.0)):
-        t = float(np.mean(res["per_kernel"][part]))
+        t = float(np.mean(res["alone"][part]))
         nbytes, flops = alg[entry], fl * T * k * H * I
         if flops / nbytes < BF16_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9):
             ach = nbytes / (t * 1e-3) / 1e9
@@ -649,7 +717,7 @@ def layer_figures(cfg, counts, res):
                  "unit": "TFLOP/s", "frac": round(ach / BF16_MFMA_PEAK_TFLOPS, 4)}
         r.update({"kernel": entry, "algorithmic_bytes": int(nbytes), "algorithmic_flops": flops,
                   "mean_launch_ms": round(t, 5),
-                  "median_launch_ms": round(float(np.median(res["per_kernel"][part])), 5),
+                  "median_launch_ms": round(float(np.median(res["alone"][part])), 5),
                   "traffic": measured_traffic(entry, cfg.name)})
         out[part] = r
     return out
@@ -730,7 +798,12 @@ def main():
     ap.add_argument("--trace-dir", default=None)
     ap.add_argument("--phases", default=None,
                     help="with --trace-dir: comma-separated workload names, in run order")
+    ap.add_argument("--show", default=None,
+                    help="with --trace-dir: the phases to print (default: all)")
     ap.add_argument("--fetch-dir", default=None)
+    ap.add_argument("--mfma-dir", default=None,
+                    help="rocprofv3 --pmc run with SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE, "
+                         "SQ_INSTS_VALU_MFMA_MOPS_BF16")
     ap.add_argument("--write-dir", default=None)
     ap.add_argument("--counts", default=None)
     ap.add_argument("--command", default=None)
