@@ -302,9 +302,13 @@ int choose_ms(int R, int E) {
 
 int tile_slots(int R, int E, int mt) { return (R < E ? R : E) + (R + mt - 1) / mt; }
 
-// workgroups launched: the tile-slot bound, capped at a few per CU
-unsigned stream_grid(int64_t slots_times_n) {
-  const int64_t cap = int64_t(4) * device_cus();
+// workgroups launched: the tile-slot bound, capped at a few per CU.  After a
+// dense pass (hi < INT_MAX) only experts below its row threshold are left,
+// often none (a uniform prefill batch): one workgroup per CU then finds that
+// out at a third of the cost of four, and walks the tiles there are
+// grid-stride.
+unsigned stream_grid(int64_t slots_times_n, int hi) {
+  const int64_t cap = int64_t(hi == INT32_MAX ? 4 : 1) * device_cus();
   return unsigned(slots_times_n < cap ? slots_times_n : cap);
 }
 
@@ -315,7 +319,7 @@ hipError_t gate_up_ms(const uint16_t* x, const int32_t* sp, const int32_t* off, 
   constexpr int NSUB = kGuNsub;
   const int R = T * k;
   const int ntile_n = (I + kWaves * 16 * NSUB - 1) / (kWaves * 16 * NSUB);
-  const unsigned grid = stream_grid(int64_t(tile_slots(R, E, 16 * MS)) * ntile_n);
+  const unsigned grid = stream_grid(int64_t(tile_slots(R, E, 16 * MS)) * ntile_n, hi);
   // 8 H bytes of scales: above 64 KB (H > 8192) the kernel's LDS limit is
   // raised to the 128 KB that H = 16384 needs
   const size_t lds = size_t(kWaves) * 2 * NSUB * 16 * (H / 32);
@@ -337,7 +341,7 @@ hipError_t down_ms(const uint16_t* h, const int32_t* off, int T, int H, int I, i
   constexpr int NSUB = kDnNsub;
   const int R = T * k;
   const int ntile_n = (H + kWaves * 16 * NSUB - 1) / (kWaves * 16 * NSUB);
-  const unsigned grid = stream_grid(int64_t(tile_slots(R, E, 16 * MS)) * ntile_n);
+  const unsigned grid = stream_grid(int64_t(tile_slots(R, E, 16 * MS)) * ntile_n, hi);
   const size_t lds = size_t(kWaves) * NSUB * 16 * (I / 32);
   k_down<MS, NSUB><<<dim3(grid), kThreads, lds, s>>>(h, off, H, I, E, c, sc, y, ntile_n,
                                                                hi);

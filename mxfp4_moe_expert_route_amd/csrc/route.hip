@@ -85,10 +85,15 @@ hipError_t launch_n(const float* logits, int T, int E, int k, int32_t* ids, floa
 //
 // Decode sizes (T <= 64): one workgroup per EPW experts and block of 8
 // tokens.  Its 256 lanes split the experts' weight rows (float4 each, 1 KB
-// strides), so every load of a row is in flight at once and each row is read
-// once per token block; each lane keeps one fma chain per (expert, token),
-// then a DPP tree per wave and the four waves' sums in order.
-template <int TB, int EPW>
+// strides) and read the block's x at the same positions; every load of a
+// lane is unconditional (rows past the block's last token re-read that
+// token) and issued before the fmas, so they are all in flight at once (with
+// a branch per token the loads of x went out one at a time, each waiting for
+// the one before: 14.7 us at 8 tokens).  Each row is read once per token
+// block; each lane keeps one fma chain per (expert, token), then a DPP tree
+// per wave and the four waves' sums in order.  NT: the weight loads carry the
+// non-temporal hint (one token block reads each row once).
+template <int TB, int EPW, bool NT>
 __global__ __launch_bounds__(256) void k_router_rows(const uint16_t* __restrict__ x,
                                                      const float* __restrict__ wr,
                                                      const float* __restrict__ bias, int T, int H,
@@ -106,34 +111,51 @@ __global__ __launch_bounds__(256) void k_router_rows(const uint16_t* __restrict_
   for (int q = 0; q < EPW; ++q)
 #pragma unroll
     for (int j = 0; j < TB; ++j) acc[q][j] = 0.f;
-#pragma unroll 6
-  for (int h = 4 * tid; h < H; h += 1024) {
-    float4 w[EPW];
+  const uint16_t* xr[TB];
 #pragma unroll
-    for (int q = 0; q < EPW; ++q)
-    {
-      // one token block reads each weight row once: non-temporal (8 tokens:
-      // 20.3 -> 19.4 us); several blocks re-read the rows from the caches
-      const float* wp = wr + size_t(e0 + min(q, ne - 1)) * H + h;
-      if (gridDim.y == 1) {
-        const f32x4 t = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(wp));
-        w[q] = make_float4(t[0], t[1], t[2], t[3]);
-      } else {
-        w[q] = *reinterpret_cast<const float4*>(wp);
+  for (int j = 0; j < TB; ++j) xr[j] = x + size_t(t0 + min(j, nt - 1)) * H;
+  const float* wrow[EPW];
+#pragma unroll
+  for (int q = 0; q < EPW; ++q) wrow[q] = wr + size_t(e0 + min(q, ne - 1)) * H;
+  // kU steps of 1024 per pass: each lane loads its 4 elements of every step
+  // (addresses clamped in range), then runs the fmas of the steps in range
+  constexpr int kU = 6;
+  for (int h0 = 4 * tid; h0 < H; h0 += kU * 1024) {
+    float4 w[kU][EPW];
+    uint2 xv[kU][TB];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int h = min(h0 + 1024 * u, H - 4);
+#pragma unroll
+      for (int q = 0; q < EPW; ++q) {
+        if constexpr (NT) {
+          const f32x4 t = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(wrow[q] + h));
+          w[u][q] = make_float4(t[0], t[1], t[2], t[3]);
+        } else {
+          w[u][q] = *reinterpret_cast<const float4*>(wrow[q] + h);
+        }
       }
-    }
 #pragma unroll
-    for (int j = 0; j < TB; ++j) {
-      if (j < nt) {
-        const uint2 xv = *reinterpret_cast<const uint2*>(x + size_t(t0 + j) * H + h);
-        const float x0 = __uint_as_float(xv.x << 16), x1 = __uint_as_float(xv.x & 0xffff0000u);
-        const float x2 = __uint_as_float(xv.y << 16), x3 = __uint_as_float(xv.y & 0xffff0000u);
+      for (int j = 0; j < TB; ++j) xv[u][j] = *reinterpret_cast<const uint2*>(xr[j] + h);
+    }
+    // keep every load of the pass ahead of the first fma (the scheduler
+    // would otherwise sink each step's loads to its fmas, one round trip each)
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const bool in = h0 + 1024 * u < H;
+#pragma unroll
+      for (int j = 0; j < TB; ++j) {
+        const uint2 v = xv[u][j];
+        const float x0 = __uint_as_float(v.x << 16), x1 = __uint_as_float(v.x & 0xffff0000u);
+        const float x2 = __uint_as_float(v.y << 16), x3 = __uint_as_float(v.y & 0xffff0000u);
 #pragma unroll
         for (int q = 0; q < EPW; ++q) {
-          acc[q][j] = fmaf(x0, w[q].x, acc[q][j]);
-          acc[q][j] = fmaf(x1, w[q].y, acc[q][j]);
-          acc[q][j] = fmaf(x2, w[q].z, acc[q][j]);
-          acc[q][j] = fmaf(x3, w[q].w, acc[q][j]);
+          float a = fmaf(x0, w[u][q].x, acc[q][j]);
+          a = fmaf(x1, w[u][q].y, a);
+          a = fmaf(x2, w[u][q].z, a);
+          a = fmaf(x3, w[u][q].w, a);
+          acc[q][j] = in ? a : acc[q][j];
         }
       }
     }
@@ -267,10 +289,11 @@ hipError_t launch_router_logits(const uint16_t* x, const float* w_router, const 
     // 15.5, four: 18.4), four when several blocks re-read the weights (21 us
     // at 64 tokens against 31)
     if (T <= 8) {
-      k_router_rows<8, 1><<<dim3(unsigned(E), 1), 256, 0, s>>>(x, w_router, bias, T, H, E, logits);
+      k_router_rows<8, 1, true><<<dim3(unsigned(E), 1), 256, 0, s>>>(x, w_router, bias, T, H, E,
+                                                                    logits);
     } else {
       const dim3 grid(unsigned((E + 3) / 4), unsigned((T + 7) / 8));
-      k_router_rows<8, 4><<<grid, 256, 0, s>>>(x, w_router, bias, T, H, E, logits);
+      k_router_rows<8, 4, false><<<grid, 256, 0, s>>>(x, w_router, bias, T, H, E, logits);
     }
   } else if (int64_t((E + 63) / 64) * ((T + 63) / 64) >= 512) {
     const dim3 grid(unsigned((E + 63) / 64), unsigned((T + 63) / 64));
