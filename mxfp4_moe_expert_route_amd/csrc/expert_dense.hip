@@ -389,34 +389,67 @@ __device__ __forceinline__ void run_item(uint8_t* lds, const Item& it, int K, in
   step(yes(), no(), s + 2, ba, bb);
   step(no(), no(), s + 3, bb, ba);
 
-  // epilogue: lane holds D[4g+v][r16]: weight row 4g+v of subtile a, token
-  // row r16 of subtile wm + kWM i
+  // Epilogue.  Lane 16g + r holds D[4g+v][r]: weight row 4g+v of subtile a,
+  // token row r of subtile wm + kWM i, so a direct store writes 16 rows x 64
+  // (y) or 32 (h) bytes per instruction; the output rows go out faster as
+  // whole pieces of a row (y: 256 bytes of four rows per instruction, h: 64
+  // bytes of sixteen rows), so each subtile is transposed through LDS first.
+  // The activation slots of stages nst - 2 and nst - 3 are free here: their
+  // last reads came before barrier nst - 2, which every wave has passed, and
+  // no load targets them any more.  Wave w uses its own part of them (y:
+  // waves 0-4 in one slot, 5-7 in the other, 16 rows of 272 bytes each; h:
+  // 16 rows of 80 bytes); a wave reads back only what it wrote, so no
+  // barrier is needed, and the next item's prologue comes after the
+  // workgroup barrier that ends this item.
+  {
+    const int sa = (nst - 2) % kRingA, sb2 = (nst - 3) % kRingA;
+    constexpr int kRowY = 272, kRowH = 80;
+    static_assert(5 * 16 * kRowY <= kAB && 3 * 16 * kRowY <= kAB && kWaves * 16 * kRowH <= kAB,
+                  "epilogue transposes fit two activation slots");
+    uint8_t* tb = GU ? lds + kLdsA + sa * kAB + wave * 16 * kRowH
+                     : lds + kLdsA + (wave < 5 ? sa : sb2) * kAB + (wave < 5 ? wave : wave - 5) * 16 * kRowY;
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int m = 16 * (wm + kWM * i) + r16;
-    if (m >= it.rows) continue;
-    const size_t row = size_t(it.row0 + m);
-    if constexpr (GU) {
-      uint16_t* h = static_cast<uint16_t*>(out);
+    for (int i = 0; i < NV; ++i) {
+      const int mb = 16 * (wm + kWM * i);            // the subtile's first tile row
+      if constexpr (GU) {
 #pragma unroll
-      for (int a = 0; a < kASub / 2; ++a) {
-        const f32x4 gv = acc[a][i];
-        const f32x4 uv = acc[a + kASub / 2][i];
-        uint32_t hv[4];
+        for (int a = 0; a < kASub / 2; ++a) {
+          const f32x4 gv = acc[a][i];
+          const f32x4 uv = acc[a + kASub / 2][i];
+          uint32_t hv[4];
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
-          hv[v] = f32_to_bf16_rne(gv[v] / (1.0f + __expf(-gv[v])) * uv[v]);
-        const int col = 128 * it.n + 8 * kASub * wn + 16 * a + 4 * g;
-        *reinterpret_cast<uint2*>(h + row * I + col) =
-            make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
-      }
-    } else {
-      float* y = static_cast<float*>(out);
+          for (int v = 0; v < 4; ++v)
+            hv[v] = f32_to_bf16_rne(gv[v] / (1.0f + __expf(-gv[v])) * uv[v]);
+          *reinterpret_cast<uint2*>(tb + r16 * kRowH + (16 * a + 4 * g) * 2) =
+              make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
+        }
+        // lane L: row L/4, h columns 8 (L%4) .. + 7 of the wave's 32
+        const uint4 hw = *reinterpret_cast<const uint4*>(tb + (lane >> 2) * kRowH + 16 * (lane & 3));
+        const int m = mb + (lane >> 2);
+        if (m < it.rows) {
+          uint16_t* h = static_cast<uint16_t*>(out);
+          const int col = 128 * it.n + 8 * kASub * wn + 8 * (lane & 3);
+          *reinterpret_cast<uint4*>(h + size_t(it.row0 + m) * I + col) = hw;
+        }
+      } else {
 #pragma unroll
-      for (int a = 0; a < kASub; ++a) {
-        const f32x4 v = acc[a][i];
-        const int col = kNT * it.n + 16 * kASub * wn + 16 * a + 4 * g;
-        *reinterpret_cast<float4*>(y + row * H + col) = make_float4(v[0], v[1], v[2], v[3]);
+        for (int a = 0; a < kASub; ++a) {
+          const f32x4 v = acc[a][i];
+          *reinterpret_cast<float4*>(tb + r16 * kRowY + (16 * a + 4 * g) * 4) =
+              make_float4(v[0], v[1], v[2], v[3]);
+        }
+        // store j, lane L: row 4j + L/16, columns 4 (L%16) .. + 3 of the wave's 64
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float4 yv =
+              *reinterpret_cast<const float4*>(tb + (4 * j + (lane >> 4)) * kRowY + 16 * (lane & 15));
+          const int m = mb + 4 * j + (lane >> 4);
+          if (m < it.rows) {
+            float* y = static_cast<float*>(out);
+            const int col = kNT * it.n + 16 * kASub * wn + 4 * (lane & 15);
+            *reinterpret_cast<float4*>(y + size_t(it.row0 + m) * H + col) = yv;
+          }
+        }
       }
     }
   }

@@ -43,6 +43,9 @@ DENSE = [
     # token rows; 192 + 20 rows, a partial subtile for every wave
     ("dense_tail_8", (200, 512, 512, 1, 1), "uniform"),
     ("dense_tail_20", (212, 1024, 512, 1, 1), "uniform"),
+    # 1024 rows per expert: 768 gate/up and 384 down items, so workgroups run
+    # several items back to back (full m-tiles and 64-row last ones)
+    ("dense_many_items", (4096, 512, 512, 32, 8), "uniform"),
 ]
 
 # shapes that take the persistent decode kernel (H, I multiples of 2048, at

@@ -25,6 +25,8 @@ CASES = [
     ("tiny_t16", None),
     ("ragged_t13", (13, 100, 7, 3)),       # H not a multiple of 256, E not of 4
     ("blocks32_t70", (70, 520, 33, 4)),    # the 32-token blocks, a ragged last block
+    ("narrow_t7", (7, 132, 19, 2)),        # one block, H % 8 == 4: 8-byte loads of x
+    ("two_pass_t6", (6, 6152, 11, 2)),     # one block, a second pass over H
     ("wide_e", (5, 64, 1024, 32)),
     ("one_expert", (9, 32, 1, 1)),
     ("verify_t8", None),
