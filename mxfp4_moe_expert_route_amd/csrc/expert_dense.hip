@@ -71,7 +71,12 @@ constexpr int kSS = 4;               // stages per weight super-stage (128 code 
 constexpr int kRingW = 2;            // weight super-stage slots
 constexpr int kWaves = 8;            // two per SIMD
 constexpr int kDThreads = kWaves * kWave;
-constexpr int kMinRows = 64;         // experts with fewer rows use the streaming kernels
+// Experts with fewer rows use the streaming kernels.  Those take 16 token
+// rows per pass over an expert's weights, the dense kernel all rows in one
+// pass at about half the streaming rate, so the dense kernel wins from three
+// passes (33 rows) on.  Measured on the 512-token Zipf batch: thresholds 17,
+// 25, 33, 41, 49, 64 give 1.304, 1.248, 1.212, 1.230, 1.271, 1.338 ms.
+constexpr int kMinRows = 33;
 constexpr int kMaxE = 1024;
 constexpr int kAB = kMT * kKS * 2;   // 24 KB of activations per stage
 constexpr int kWSlot = kNT * kKS * kSS / 2;   // 32 KB of codes per super-stage

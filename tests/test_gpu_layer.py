@@ -32,6 +32,10 @@ SMALL = [
     ("wide_h16384", (4, 16384, 64, 4, 2)),     # largest H: 128 KB of scales in the streaming kernel
 ]
 
+# experts with at least this many rows take the dense kernel (192-row items),
+# the others the streaming kernels (16-row items)
+DENSE_MIN_ROWS = 33
+
 # shapes that take the LDS-tiled dense kernel (H, I multiples of 512, many
 # rows per expert): one tile per expert, several tiles per expert, and a
 # skewed mix where only the popular experts are dense
@@ -51,11 +55,15 @@ DENSE = [
 # shapes that take the persistent decode kernel (H, I multiples of 2048, at
 # most 16 rows per expert on average): a single token, experts split into
 # several 16-row tiles by skewed routing, and enough units that each
-# workgroup's run crosses several units and tiles
+# workgroup's run crosses several units and tiles.  decode_zipf_tiles also
+# launches the dense kernel, which takes its two experts of 34 and 51 rows;
+# decode_zipf_deep (fewer than 8 rows per touched expert: no dense launch)
+# leaves an expert of 54 rows, four 16-row tiles, to the decode kernel.
 DECODE = [
     ("decode_one_tok", (1, 2048, 2048, 8, 4), "uniform"),
     ("decode_zipf_tiles", (64, 2048, 2048, 16, 2), "zipf"),
     ("decode_runs", (64, 2048, 2048, 32, 8), "uniform"),
+    ("decode_zipf_deep", (64, 2048, 2048, 32, 2), "zipf"),
 ]
 
 
@@ -104,7 +112,7 @@ def test_layer_dense_path_every_token(mm, name, shape, routing):
     b, ref, _ = check_layer(cfg, d["x_bits"], d["logits"], d, upload_weights(d))
     counts = b.counts.cpu().numpy()
     say("  rows per expert: min %d max %d" % (counts.min(), counts.max()))
-    assert counts.max() >= 64                        # at least one expert takes the dense kernel
+    assert counts.max() >= DENSE_MIN_ROWS            # at least one expert takes the dense kernel
 
 
 @pytest.mark.parametrize("name,shape,routing", DECODE, ids=[d[0] for d in DECODE])
@@ -169,7 +177,7 @@ def test_page_shaped_every_block_written_and_sampled(mm, name):
     h, y and the output is written (the buffers start as NaN), and one element
     of every work item of every kernel is checked against the oracle:
       h    every block of an expert's rows x 128 columns (gate/up items: 192
-           token rows for experts with at least 64 rows, 16 for the others, by
+           token rows for experts with at least 33 rows, 16 for the others, by
            128 gate columns with their up columns);
       y    every block of those rows x 256 output features (down items), from
            the GPU's own h row;
@@ -206,7 +214,7 @@ def test_page_shaped_every_block_written_and_sampled(mm, name):
     rows, cols = [], []
     for e in range(E):
         n_e = int(offsets[e + 1] - offsets[e])
-        blk = 192 if n_e >= 64 else 16
+        blk = 192 if n_e >= DENSE_MIN_ROWS else 16
         for r0 in range(0, n_e, blk):
             nr = min(blk, n_e - r0)
             for c0 in range(0, I, 128):
@@ -243,7 +251,7 @@ def test_page_shaped_every_block_written_and_sampled(mm, name):
     rows, cols = [], []
     for e in range(E):
         n_e = int(offsets[e + 1] - offsets[e])
-        blk = 192 if n_e >= 64 else 16
+        blk = 192 if n_e >= DENSE_MIN_ROWS else 16
         for r0 in range(0, n_e, blk):
             nr = min(blk, n_e - r0)
             for c0 in range(0, H, 256):
