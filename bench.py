@@ -9,9 +9,10 @@ expert weights alternate between steps so the 256 MB last-level cache cannot
 serve them.
 
 Each workload runs --warmup steps, then more until --warm-seconds have passed
-(the clocks settle under sustained load), then three timed passes of --steps
+(the clocks settle under sustained load), then four timed passes of --steps
 steps: the headline region (two events around all steps), per-step events
-(median / p10 / p90) and events around every entry point (per-kernel times).
+(median / p10 / p90), events around every entry point (per-kernel times) and
+events around each contraction alone (the roofline's launch times).
 The verify_t8 run also times the same step through the persistent decode
 layer entry point (one kernel), then verify_t64, zipf_t512 and prefill_t8192
 on the same weights with the same flags.
