@@ -50,6 +50,10 @@ DENSE = [
     # 1024 rows per expert: 768 gate/up and 384 down items, so workgroups run
     # several items back to back (full m-tiles and 64-row last ones)
     ("dense_many_items", (4096, 512, 512, 32, 8), "uniform"),
+    # three scale chunks per gate/up item (an odd count above one), and the
+    # largest hidden size the decode kernel also takes
+    ("dense_odd_chunks", (400, 1536, 512, 4, 2), "uniform"),
+    ("dense_h8192", (1024, 8192, 1024, 8, 2), "uniform"),
 ]
 
 # shapes that take the persistent decode kernel (H, I multiples of 2048, at
