@@ -56,6 +56,10 @@
 // xor-swizzled ones, read at about half that rate on gfx950.  A weight
 // super-stage keeps each row's 128 bytes together, 16-byte block b in slot
 // b ^ ((row >> 1) & 7), which makes the 8-byte code reads conflict-free.
+//
+// The epilogue goes through LDS too: a wave's 16-row output subtile is
+// written to a free activation slot and read back row-major, so each store
+// writes whole pieces of output rows rather than 16 rows x 64 bytes.
 #include <type_traits>
 
 #include "common.hpp"
