@@ -62,12 +62,15 @@ DENSE = [
 # workgroup's run crosses several units and tiles.  decode_zipf_tiles also
 # launches the dense kernel, which takes its two experts of 34 and 51 rows;
 # decode_zipf_deep (fewer than 8 rows per touched expert: no dense launch)
-# leaves an expert of 54 rows, four 16-row tiles, to the decode kernel.
+# leaves an expert of 54 rows, four 16-row tiles, to the decode kernel;
+# decode_h8192 runs gate/up at the largest K the kernel takes (8192),
+# with experts of 17..21 rows in two tiles.
 DECODE = [
     ("decode_one_tok", (1, 2048, 2048, 8, 4), "uniform"),
     ("decode_zipf_tiles", (64, 2048, 2048, 16, 2), "zipf"),
     ("decode_runs", (64, 2048, 2048, 32, 8), "uniform"),
     ("decode_zipf_deep", (64, 2048, 2048, 32, 2), "zipf"),
+    ("decode_h8192", (32, 8192, 2048, 24, 4), "zipf"),
 ]
 
 
@@ -129,6 +132,8 @@ def test_layer_decode_path_every_token(mm, name, shape, routing):
     b, ref, _ = check_layer(cfg, d["x_bits"], d["logits"], d, upload_weights(d))
     counts = b.counts.cpu().numpy()
     say("  rows per expert: min %d max %d" % (counts.min(), counts.max()))
+    if name == "decode_h8192":
+        assert counts.max() > 16                     # an expert in two tiles
 
 
 def test_layer_is_deterministic(mm):
