@@ -93,11 +93,17 @@ template <int NPER>
 __device__ __forceinline__ void route_token(const float* __restrict__ row, int E, int k,
                                             int& my_id, float& my_w) {
   const int lane = lane_id();
+  // every load is unconditional (lanes past E re-read the last logit) and
+  // issued before the first key is built, so they are in flight together; a
+  // load per branch went out one at a time, each waiting for the one before
+  float v[NPER];
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) v[i] = row[min(lane + kWave * i, E - 1)];
   uint64_t key[NPER];
 #pragma unroll
   for (int i = 0; i < NPER; ++i) {
     const int e = lane + kWave * i;
-    key[i] = (e < E) ? (uint64_t(order_key(row[e])) << 32) | uint64_t(0xffffffffu - uint32_t(e))
+    key[i] = (e < E) ? (uint64_t(order_key(v[i])) << 32) | uint64_t(0xffffffffu - uint32_t(e))
                      : 0ull;
   }
   my_id = 0;
