@@ -29,6 +29,13 @@ FLAGS = [
 ]
 
 
+# per-source flags.  decode_layer.hip: no atomic aggregation across a wave
+# (the kernel's atomics run on one lane, and the aggregated form reads each
+# answer at once, which would put every queue claim's round trip on the path
+# of the stage barriers)
+FILE_FLAGS = {"decode_layer.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
+
+
 def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -48,7 +55,8 @@ def build(verbose=False, jobs=None):
     objs = [os.path.join(BUILD, os.path.basename(s)[:-4] + ".o") for s in srcs]
     jobs = jobs or min(len(srcs), os.cpu_count() or 4, 16)
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        list(ex.map(lambda so: _run([HIPCC] + FLAGS + ["-c", so[0], "-o", so[1]], verbose),
+        list(ex.map(lambda so: _run([HIPCC] + FLAGS + FILE_FLAGS.get(os.path.basename(so[0]), [])
+                                    + ["-c", so[0], "-o", so[1]], verbose),
                     zip(srcs, objs)))
     tmp = LIB + ".tmp%d" % os.getpid()
     _run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs, verbose)

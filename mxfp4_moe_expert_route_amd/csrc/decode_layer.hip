@@ -64,6 +64,10 @@ constexpr int kWsWords = kWsDn + kDLMaxNB;
 constexpr size_t kWsBytes = 4096;
 static_assert(kWsWords * 4 <= int(kWsBytes), "workspace words");
 
+// s_waitcnt immediate that waits for lgkmcnt == 0 and nothing else (gfx9
+// layout: vmcnt and expcnt at their maxima)
+#define MXM_LGKMCNT0 ((15 | (3 << 14)) | (7 << 4))
+
 // a wait for a tile's gate/up units polls at most this many times (each poll
 // is a device-scope load, about a microsecond, then a short sleep): about a
 // second, far beyond any real wait (at most one phase, ~0.1 ms)
@@ -128,8 +132,11 @@ __device__ __forceinline__ uint64_t load_dev64(const void* p) {
 
 // The units of one phase: a queue in tile order (unit d: tile d / per,
 // column block d % per), claimed one unit ahead.  This workgroup's unit i is
-// in descriptor slot i % 4 in LDS, written by the scale loader at the first
-// stage of unit i - 1 (by thread 0 for unit 0).
+// in descriptor slot i % 4 in LDS (thread 0 writes unit 0's).  The scale
+// loader takes unit i's number from the queue at the first stage of unit
+// i - 1 and writes its slot at stage S - 9, so the atomic's round trip is
+// off the path of the stage barriers (this file is built without the
+// compiler's atomic aggregation, which would wait for the answer at once).
 struct Units {
   const uint8_t* lds;
   uint32_t* head;              // the queue's next unit (workspace word)
@@ -140,9 +147,11 @@ struct Units {
     return Unit{v.x, v.y, v.z, v.w & 0xffff, v.w >> 16};
   }
 
-  // claim the next unit of the queue into slot i % 4 (one lane)
-  __device__ __forceinline__ void claim(int i) const {
-    const int d = int(add_dev(head, 1u));
+  // one lane: the queue's next unit number
+  __device__ __forceinline__ int take() const { return int(add_dev(head, 1u)); }
+
+  // one lane: unit number d (past the end: the end marker) into slot i % 4
+  __device__ __forceinline__ void put(int i, int d) const {
     int4v v{-1, 0, 0, 1};
     if (d < total) {
       const int tile = d / per;
@@ -151,6 +160,9 @@ struct Units {
     }
     *reinterpret_cast<int4v*>(const_cast<uint8_t*>(lds) + kLSlots + 16 * (i & 3)) = v;
   }
+
+  // one lane: take the next unit into slot i % 4 now
+  __device__ __forceinline__ void claim(int i) const { put(i, take()); }
 };
 
 // Unit completion, sent by thread 0 once every MFMA wave's stores of the unit
@@ -205,9 +217,16 @@ __device__ Unit run_phase(uint8_t* lds, const Layer& L, const Units& src, uint8_
     for (int j = 0;; ++j) {
       const Unit u = src.get(j);
       if (u.e < 0) break;
+      int nd = 0;                                    // lane 0: unit j + 1's number
       for (int s = 0; s < S; ++s) {
         wg_barrier();
-        if (s == 0 && lane == 0) src.claim(j + 1);  // take unit j + 1 from the queue
+        // unit j + 1: its number at stage 0, its slot at stage S - 9 (the
+        // activation loader reads it at S - 7, the code loaders at S - 4)
+        if (s == 0 && lane == 0) nd = src.take();
+        if (s == S - 9 && lane == 0) {
+          src.put(j + 1, nd);
+          __builtin_amdgcn_s_waitcnt(MXM_LGKMCNT0);
+        }
         // the unit's last scale read is at its stage S - 8; the next unit's
         // scales go out in three parts at stages S - 7 .. S - 5
         if (s == S - 7) un = src.get(j + 1);
@@ -224,7 +243,7 @@ __device__ Unit run_phase(uint8_t* lds, const Layer& L, const Units& src, uint8_
     const uint8_t* act = reinterpret_cast<const uint8_t*>(GU ? L.x : L.h);
     const int nch = K / kChunkK;
     int tok = 0, tok_row0 = -1;
-    auto issue_acts = [&](const Unit& u, int kc) {
+    auto issue_acts = [&](const Unit& u, int kc, uint32_t seen) {
       if constexpr (GU) {
         if (u.row0 != tok_row0) {
           tok_row0 = u.row0;
@@ -232,8 +251,9 @@ __device__ Unit run_phase(uint8_t* lds, const Layer& L, const Units& src, uint8_
         }
       } else {
         // the tile's h rows are written by other workgroups: wait (bounded)
-        // until all its gate/up units are in
-        if (kc == 0) {
+        // until all its gate/up units are in (`seen`: the count read when the
+        // unit became known, usually the whole tile already)
+        if (kc == 0 && seen < uint32_t(L.ntg)) {
           const uint32_t* cnt = L.ws + kWsGu + u.tile;
           int polls = 0;
           while (load_dev(cnt) < uint32_t(L.ntg)) {
@@ -258,15 +278,28 @@ __device__ Unit run_phase(uint8_t* lds, const Layer& L, const Units& src, uint8_
                                          GU ? 0 : kAuxSC1);
       }
     };
-    // next chunk to issue: chunk ca of unit ja
+    // next chunk to issue: chunk ca of unit ja.  Down: when unit ja + 1
+    // becomes known (as the last chunk of unit ja goes out) its tile's count
+    // is loaded, the last load of the wave; the wait at the end of that
+    // chunk-group leaves it outstanding, and it is looked at when the unit's
+    // first chunk goes out, four stages later.
     int ja = 0, ca = 0;
     Unit ua = src.get(0);
+    uint32_t seen = 0;                             // down: ua's tile count, loaded early
+    bool seen_pending = false;
     auto issue_next = [&]() {
       if (ua.e < 0) return;
-      issue_acts(ua, ca);
+      issue_acts(ua, ca, seen);
       if (++ca == nch) {
         ca = 0;
         ua = src.get(++ja);
+        if constexpr (!GU) {
+          seen = 0;
+          if (ua.e >= 0) {
+            seen = load_dev(L.ws + kWsGu + ua.tile);
+            seen_pending = true;
+          }
+        }
       }
     };
     issue_next();
@@ -280,7 +313,14 @@ __device__ Unit run_phase(uint8_t* lds, const Layer& L, const Units& src, uint8_
         // a chunk's rows are read at its first stage; the next chunk goes
         // out three stages before its first stage, after that read
         if (((q + 3) & 3) == 0) issue_next();
-        if (((q + 1) & 3) == 0) __builtin_amdgcn_s_waitcnt(MXM_VMCNT(0));
+        if (((q + 1) & 3) == 0) {
+          if (seen_pending) {
+            __builtin_amdgcn_s_waitcnt(MXM_VMCNT(1));   // all but the count load
+            seen_pending = false;
+          } else {
+            __builtin_amdgcn_s_waitcnt(MXM_VMCNT(0));
+          }
+        }
       }
     }
     return pending;
@@ -339,6 +379,11 @@ __device__ Unit run_phase(uint8_t* lds, const Layer& L, const Units& src, uint8_
   uint32_t sc4[2][4];
   uint4 xb[4][4];
   int q = 0;
+  // down, thread 0: the previous unit's column-block count, sent at stage 2
+  // and looked at at stage 7, so the atomic's round trip is off the path of
+  // the stage barriers
+  uint32_t blk_count = 0;
+  int blk_nt = -1;
   for (int j = 0;; ++j) {
     const Unit u = src.get(j);
     if (u.e < 0) break;
@@ -354,13 +399,25 @@ __device__ Unit run_phase(uint8_t* lds, const Layer& L, const Units& src, uint8_
           // the barrier of stage 2 (every MFMA wave has waited by then)
           if (st8 == 1) __builtin_amdgcn_s_waitcnt(MXM_VMCNT(0));
           if (st8 == 2) {
-            if (tid == 0 && signal_unit<GU>(L, pending)) {
-              int* nc = reinterpret_cast<int*>(lds + kLMisc + 4);
-              reinterpret_cast<int*>(comb)[*nc] = pending.nt;
-              *nc += 1;
+            if (tid == 0) {
+              if constexpr (GU) {
+                signal_unit<GU>(L, pending);
+              } else {
+                blk_count = add_dev(L.ws + kWsDn + pending.nt, 1u);
+                blk_nt = pending.nt;
+              }
             }
             pending = end_unit();
           }
+        }
+        if (!GU && s0 == 0 && st8 == 7 && tid == 0 && blk_nt >= 0) {
+          // the previous unit completed its column block: combine it at the end
+          if (blk_count + 1u == uint32_t(L.ntiles)) {
+            int* nc = reinterpret_cast<int*>(lds + kLMisc + 4);
+            reinterpret_cast<int*>(comb)[*nc] = blk_nt;
+            *nc += 1;
+          }
+          blk_nt = -1;
         }
         if (st8 == 0) read_scales(scb, nblk, w, (s0 + st8) >> 2, sc4);   // this chunk and the next
         if (rg == 0) read_acts(actb, u.rows, xb);
