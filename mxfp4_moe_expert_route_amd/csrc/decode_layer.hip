@@ -379,7 +379,7 @@ __device__ Unit run_phase(uint8_t* lds, const Layer& L, const Units& src, uint8_
   uint32_t sc4[2][4];
   uint4 xb[4][4];
   int q = 0;
-  // down, thread 0: the previous unit's column-block count, sent at stage 2
+  // down, thread 0: the previous unit's column-block count, sent at stage 4
   // and looked at at stage 7, so the atomic's round trip is off the path of
   // the stage barriers
   uint32_t blk_count = 0;
@@ -395,10 +395,12 @@ __device__ Unit run_phase(uint8_t* lds, const Layer& L, const Units& src, uint8_
         const int par = st8 >> 2, rg = st8 & 3;
         wg_barrier();
         if (pending.e >= 0 && s0 == 0) {
-          // the previous unit's stores: complete by stage 1, signalled after
-          // the barrier of stage 2 (every MFMA wave has waited by then)
-          if (st8 == 1) __builtin_amdgcn_s_waitcnt(MXM_VMCNT(0));
-          if (st8 == 2) {
+          // the previous unit's stores: complete by stage 3, signalled after
+          // the barrier of stage 4 (every MFMA wave has waited by then).
+          // Waiting at stage 1 instead cost 0.3-1 us per call: a store
+          // written through to memory can take longer than a stage.
+          if (st8 == 3) __builtin_amdgcn_s_waitcnt(MXM_VMCNT(0));
+          if (st8 == 4) {
             if (tid == 0) {
               if constexpr (GU) {
                 signal_unit<GU>(L, pending);
