@@ -9,12 +9,15 @@
 namespace mxm {
 namespace {
 
-// One workgroup per (token, 2048 columns): the token's k rows and weights are
-// read once into LDS, then every thread issues its 2k row loads together (two
-// 16-byte loads per row, 1024 columns apart; no branch between them: a
-// dropped pair reads row 0 and its term is not added) and accumulates them in
-// slot order.  Each row of y is read once, so the loads carry the
-// non-temporal hint (at 8192 tokens x top-8: 380 -> 318 us).
+// One workgroup per (token, CW columns): the token's k rows and weights are
+// read once into LDS, then every thread issues its row loads together (one
+// 16-byte load per row, or two 1024 columns apart when CW = 2048; no branch
+// between them: a dropped pair reads row 0 and its term is not added) and
+// accumulates them in slot order.  Each row of y is read once, so the loads
+// carry the non-temporal hint (at 8192 tokens x top-8: 380 -> 318 us).  A
+// small batch takes CW = 1024, twice the workgroups (8 tokens: 48 instead of
+// 24; the layer step 0.6 us shorter).
+template <int CW>
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y,
                                                  const float* __restrict__ w,
                                                  const int32_t* __restrict__ pair_to_row, int T,
@@ -27,8 +30,8 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y,
     sw[threadIdx.x] = w[int64_t(t) * k + threadIdx.x];
   }
   __syncthreads();
-  const int c0 = blockIdx.y * 2048 + threadIdx.x * 4;      // columns c0 and c0 + 1024
-  const bool in1 = c0 + 1024 < H;
+  const int c0 = blockIdx.y * CW + threadIdx.x * 4;        // columns c0 (and c0 + 1024)
+  const bool in1 = CW == 2048 && c0 + 1024 < H;
   if (c0 >= H) return;
   float4 acc0 = make_float4(0.f, 0.f, 0.f, 0.f), acc1 = acc0;
   for (int j0 = 0; j0 < k; j0 += 8) {
@@ -61,8 +64,12 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y,
 
 hipError_t launch_combine(const float* y, const float* w, const int32_t* pair_to_row, int T,
                           int H, int k, float* out, hipStream_t s) {
-  k_combine<<<dim3(unsigned(T), unsigned((H + 2047) / 2048)), 256, 0, s>>>(y, w, pair_to_row, T,
-                                                                          H, k, out);
+  if (int64_t(T) * ((H + 2047) / 2048) < 256)
+    k_combine<1024><<<dim3(unsigned(T), unsigned((H + 1023) / 1024)), 256, 0, s>>>(
+        y, w, pair_to_row, T, H, k, out);
+  else
+    k_combine<2048><<<dim3(unsigned(T), unsigned((H + 2047) / 2048)), 256, 0, s>>>(
+        y, w, pair_to_row, T, H, k, out);
   return hipGetLastError();
 }
 
