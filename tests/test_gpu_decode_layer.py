@@ -124,3 +124,46 @@ def test_decode_layer_page_shaped_repeated(mm):
             mx = np.abs(out - want).max() / np.sqrt(np.mean(want ** 2))
             say("  oracle on 2 tokens: rel-L2 %.3g, max|d|/RMS %.3g" % (rel, mx))
             assert rel <= 2e-3 and mx <= 1e-2
+
+
+def test_decode_layer_two_streams(mm):
+    """Two persistent layers in flight at once, on two streams with their own
+    workspaces and buffers (an 8-token and a 16-token batch of the page-shaped
+    layer, three rounds with no synchronisation between).  The second grid
+    finds the CUs held by the first, so its workgroups start as the first's
+    end (a kernel trace of this test shows the grids of the two streams
+    overlapping for about 250 us): the kernel must not depend on its
+    workgroups being resident together.  Every output equals moe_mxfp4_layer's bit for bit, no bounded
+    wait gives up, and both workspaces come back zero-filled."""
+    whost, wdev = page_layer_weights()
+    base = workloads.CONFIGS["verify_t8"]
+    c16 = workloads.custom_config("verify_t16_two_streams", 970, 16, base.H, base.I, base.E,
+                                  base.k)
+    c16 = dataclasses.replace(c16, layer_id=base.lid)
+    runs = []
+    for cfg in (base, c16):
+        xb = workloads.gen_x_bits(cfg, 0)
+        lg = workloads.gen_logits(cfg, xb, 0)
+        x, logits = dev_bf16(xb), torch.from_numpy(lg).to(DEV)
+        ws = mm.decode_layer_workspace(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, DEV)
+        b = mm.LayerBuffers(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, DEV)
+        runs.append((cfg, x, logits, ws, b, torch.cuda.Stream(device=DEV)))
+    torch.cuda.synchronize()
+    for rnd in range(3):
+        for cfg, x, logits, ws, b, s in runs:
+            with torch.cuda.stream(s):
+                mm.moe_mxfp4_decode_layer(x, logits, cfg.k, wdev["w13_codes"], wdev["w13_scales"],
+                                          wdev["w2_codes"], wdev["w2_scales"], ws, buffers=b)
+    torch.cuda.synchronize()
+    for cfg, x, logits, ws, b, s in runs:
+        say("two streams: T=%d" % cfg.T)
+        ref = mm.moe_mxfp4_layer(x, logits, cfg.k, wdev["w13_codes"], wdev["w13_scales"],
+                                 wdev["w2_codes"], wdev["w2_scales"])
+        torch.cuda.synchronize()
+        for name in OUTPUTS:
+            a = getattr(b, name).view(torch.uint8).cpu().numpy()
+            r = getattr(ref, name).view(torch.uint8).cpu().numpy()
+            assert np.array_equal(a, r), "T=%d: %s differs from moe_mxfp4_layer" % (cfg.T, name)
+        wsh = ws.cpu().numpy().view(np.uint32)
+        assert wsh[2] == 0, "T=%d: a bounded wait in the kernel gave up" % cfg.T
+        assert not wsh.any(), "T=%d: workspace not left zero-filled" % cfg.T
