@@ -815,8 +815,9 @@ def main():
         return
 
     if args.gpus != 1:
-        print("bench.py: this build runs on exactly one GPU; --gpus %d is not supported "
-              "(the layer is measured on one MI355X)" % args.gpus, file=sys.stderr)
+        print("bench.py: the layer is measured on exactly one GPU; --gpus %d is not supported "
+              "(one MI355X runs the whole layer; sharding is not implemented)" % args.gpus,
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
